@@ -1,0 +1,122 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of an oracle function (on the CPU,
+by monkeypatching) and checks that at least one pin then fails. This shows
+that the pins constrain the oracle rather than restate it.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.experts as ox
+import oracle.routing as orr
+from oracle import e4m3
+
+import test_oracle_e4m3 as te
+import test_oracle_experts as tx
+import test_oracle_routing as tr
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def _group_scores_max(key, n_group):
+    T, E = key.shape
+    return np.asarray(key).reshape(T, n_group, E // n_group).max(axis=2)
+
+
+def _group_scores_top3(key, n_group):
+    T, E = key.shape
+    b = np.sort(np.asarray(key).reshape(T, n_group, E // n_group), axis=2)
+    return b[:, :, -1] + b[:, :, -2] + b[:, :, -3]
+
+
+def _order_unstable(values):
+    # ties to the higher index
+    v = np.asarray(values)
+    return np.argsort(-v[:, ::-1], axis=1, kind="stable")[:, :] * -1 + (v.shape[1] - 1)
+
+
+def test_group_score_as_max_is_caught(monkeypatch):
+    monkeypatch.setattr(orr, "group_scores", _group_scores_max)
+    assert _fails(tr.test_golden_group_score_is_top2_sum) or _fails(tr.test_bruteforce_group_subsets_full_shape)
+
+
+def test_group_score_top3_is_caught(monkeypatch):
+    monkeypatch.setattr(orr, "group_scores", _group_scores_top3)
+    assert _fails(tr.test_bruteforce_group_subsets_full_shape)
+
+
+def test_tie_to_higher_index_is_caught(monkeypatch):
+    monkeypatch.setattr(orr, "_order_desc", _order_unstable)
+    assert _fails(tr.test_all_equal_keys_tie_rule)
+
+
+def test_bias_in_weights_is_caught(monkeypatch):
+    real = orr.route
+
+    def route_bias_in_w(x, rw, b, n_group=8, topk_group=4, top_k=8):
+        r = real(x, rw, b, n_group, topk_group, top_k)
+        k = np.take_along_axis(r["key"], r["idx"], 1)
+        r["w"] = k / k.sum(1, keepdims=True)
+        return r
+
+    monkeypatch.setattr(orr, "route", route_bias_in_w)
+    monkeypatch.setattr(oracle, "route", route_bias_in_w)
+    assert _fails(tr.test_forced_set_by_bias)
+
+
+def test_outside_groups_zeroed_is_caught(monkeypatch):
+    real = orr.select_from_keys
+
+    def zero_fill(key, n_group, topk_group, top_k):
+        r = real(key, n_group, topk_group, top_k)
+        masked = np.where(np.isfinite(r["masked_key"]), r["masked_key"], 0.0)
+        r["idx"] = np.argsort(-masked, axis=1, kind="stable")[:, :top_k]
+        return r
+
+    monkeypatch.setattr(oracle, "select_from_keys", zero_fill)
+    assert _fails(tr.test_outside_kept_groups_never_chosen_even_with_negative_keys)
+
+
+def test_missing_scale_is_caught(monkeypatch):
+    real = ox._combine
+    monkeypatch.setattr(ox, "_combine", lambda x, idx, w, rsf, g, fp8: real(x, idx, w, 1.0, g, fp8))
+    assert _fails(tx.test_identical_experts_closed_form)
+
+
+def test_silu_sign_is_caught(monkeypatch):
+    monkeypatch.setattr(ox, "silu", lambda v: np.asarray(v) / (1.0 + np.exp(np.asarray(v))))
+    assert _fails(tx.test_expert_matches_torch_swiglu)
+
+
+def test_gate_up_swapped_is_caught(monkeypatch):
+    real = ox.expert_ffn
+    monkeypatch.setattr(oracle, "expert_ffn", lambda x, g, u, d, quantize_h=False: real(x, u, g, d, quantize_h))
+    assert _fails(tx.test_expert_matches_torch_swiglu)
+
+
+def test_round_half_up_is_caught(monkeypatch):
+    real_rint = np.rint
+
+    class NP:
+        def __getattr__(self, k):
+            if k == "rint":
+                return lambda a: np.floor(np.asarray(a) + 0.5)
+            return getattr(np, k)
+
+    monkeypatch.setattr(e4m3, "np", NP())
+    assert _fails(te.test_midpoints_against_torch)
+    assert real_rint is np.rint
+
+
+def test_wrong_exponent_bias_is_caught(monkeypatch):
+    real_decode = e4m3.decode
+    monkeypatch.setattr(e4m3, "decode", lambda c: real_decode(c) * 2.0)
+    assert _fails(te.test_known_codes)

@@ -1,0 +1,194 @@
+"""Beam sparse-MoE block on MI355X (gfx950): Python binding of libbeam_moe.so.
+
+Argument marshalling only. Every step of the block (router logits, group-
+limited selection, permutation, expert GEMMs, combine) runs in the HIP
+kernels behind the C ABI declared in include/beam_moe.h; torch supplies
+device memory and the current stream. If the library is missing the calls
+raise instead of falling back to anything else.
+
+Names follow the Beam model doc's config fields: n_group, topk_group,
+routed_scaling_factor (transformers model doc "Beam", "Overview").
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbeam_moe.so")
+
+BEAM_OK, BEAM_ERR_NULL, BEAM_ERR_CONFIG, BEAM_ERR_SHAPE = 0, 1, 2, 3
+BEAM_ERR_DTYPE, BEAM_ERR_ALIGN, BEAM_ERR_WORKSPACE, BEAM_ERR_HIP = 4, 5, 6, 7
+BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
+
+EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_forward",
+            "beam_moe_status_string")
+
+
+class BeamMoeConfig(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("intermediate", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("n_group", ctypes.c_int32),
+        ("topk_group", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("routed_scaling_factor", ctypes.c_float),
+        ("x_dtype", ctypes.c_int32),
+        ("w_dtype", ctypes.c_int32),
+    ]
+
+
+class BeamMoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {status_string(status)}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (loaded once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m group_limited_routing_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        cfgp = ctypes.POINTER(BeamMoeConfig)
+        L.beam_moe_workspace_bytes.argtypes = [cfgp, i32]
+        L.beam_moe_workspace_bytes.restype = sz
+        L.beam_moe_route.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.beam_moe_route.restype = ctypes.c_int
+        L.beam_moe_forward.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, vp, sz, vp]
+        L.beam_moe_forward.restype = ctypes.c_int
+        L.beam_moe_status_string.argtypes = [i32]
+        L.beam_moe_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().beam_moe_status_string(int(status)).decode()
+
+
+_X_DTYPES = {torch.float32: BEAM_F32, torch.bfloat16: BEAM_BF16}
+_W_DTYPES = {torch.bfloat16: BEAM_BF16, torch.float8_e4m3fn: BEAM_FP8_E4M3}
+
+
+def make_config(hidden, intermediate, n_experts=256, n_group=8, topk_group=4, top_k=8,
+                routed_scaling_factor=2.5, x_dtype=torch.bfloat16, w_dtype=torch.bfloat16):
+    if x_dtype not in _X_DTYPES or w_dtype not in _W_DTYPES:
+        raise TypeError(f"unsupported dtypes x={x_dtype} w={w_dtype}")
+    return BeamMoeConfig(hidden, intermediate, n_experts, n_group, topk_group, top_k,
+                         routed_scaling_factor, _X_DTYPES[x_dtype], _W_DTYPES[w_dtype])
+
+
+def workspace_bytes(cfg, T):
+    return int(lib().beam_moe_workspace_bytes(ctypes.byref(cfg), int(T)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtypes, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _workspace(cfg, T, device, workspace):
+    need = workspace_bytes(cfg, T)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def route(x, router_w, expert_bias, *, n_group=8, topk_group=4, top_k=8,
+          return_logits=False, return_counts=False, workspace=None, stream=None):
+    """Router only. Returns dict(topk_idx [T, k] int32, topk_w [T, k] fp32,
+    router_logits [T, E] fp32 or None, expert_counts [E] int32 or None)."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    dev = x.device
+    _check(x, "x", (T, H), (torch.float32, torch.bfloat16), dev)
+    _check(router_w, "router_w", (E, H), (torch.float32,), dev)
+    _check(expert_bias, "expert_bias", (E,), (torch.float32,), dev)
+    cfg = make_config(H, 128, E, n_group, topk_group, top_k, 1.0, x.dtype, torch.bfloat16)
+    idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if return_logits else None
+    counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
+    ws = _workspace(cfg, T, dev, workspace)
+    st = lib().beam_moe_route(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
+                              _ptr(idx), _ptr(w), _ptr(logits), _ptr(counts), _ptr(ws),
+                              ws.numel(), _stream(dev, stream))
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_route")
+    return {"topk_idx": idx, "topk_w": w, "router_logits": logits, "expert_counts": counts}
+
+
+def forward(x, router_w, expert_bias, w_gate, w_up, w_down, *, scales=None, n_group=8,
+            topk_group=4, top_k=8, routed_scaling_factor=2.5, out=None, return_routing=False,
+            return_logits=False, workspace=None, stream=None):
+    """The whole MoE block. ``scales`` = (w_gate_scale, w_up_scale, w_down_scale)
+    for fp8 weights. Returns out [T, H] (x's dtype), or (out, routing dict) with
+    ``return_routing``."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    I = w_gate.shape[1]
+    dev = x.device
+    wdt = (torch.bfloat16, torch.float8_e4m3fn)
+    _check(x, "x", (T, H), (torch.float32, torch.bfloat16), dev)
+    _check(router_w, "router_w", (E, H), (torch.float32,), dev)
+    _check(expert_bias, "expert_bias", (E,), (torch.float32,), dev)
+    _check(w_gate, "w_gate", (E, I, H), wdt, dev)
+    _check(w_up, "w_up", (E, I, H), (w_gate.dtype,), dev)
+    _check(w_down, "w_down", (E, H, I), (w_gate.dtype,), dev)
+    sg = su = sd = None
+    if w_gate.dtype == torch.float8_e4m3fn:
+        if scales is None:
+            raise ValueError("fp8 weights need (w_gate_scale, w_up_scale, w_down_scale)")
+        sg, su, sd = scales
+        _check(sg, "w_gate_scale", (E, I), (torch.float32,), dev)
+        _check(su, "w_up_scale", (E, I), (torch.float32,), dev)
+        _check(sd, "w_down_scale", (E, H), (torch.float32,), dev)
+    cfg = make_config(H, I, E, n_group, topk_group, top_k, routed_scaling_factor, x.dtype,
+                      w_gate.dtype)
+    if out is None:
+        out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    else:
+        _check(out, "out", (T, H), (x.dtype,), dev)
+    idx = w = counts = logits = None
+    if return_routing:
+        idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+        counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    if return_logits:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ws = _workspace(cfg, T, dev, workspace)
+    st = lib().beam_moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
+                                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sg), _ptr(su),
+                                _ptr(sd), _ptr(out), _ptr(idx), _ptr(w), _ptr(counts),
+                                _ptr(logits), _ptr(ws), ws.numel(), _stream(dev, stream))
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_forward")
+    if return_routing or return_logits:
+        return out, {"topk_idx": idx, "topk_w": w, "expert_counts": counts,
+                     "router_logits": logits}
+    return out

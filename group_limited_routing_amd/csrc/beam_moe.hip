@@ -1,0 +1,289 @@
+// C ABI of the Beam MoE block: argument checks, workspace layout, and the
+// order of kernel launches. See include/beam_moe.h for the contract.
+#include "../../include/beam_moe.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+Layout make_layout(const Shape& s) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t T = (size_t)s.T, k = (size_t)s.top_k, E = (size_t)s.E;
+  const size_t H = (size_t)s.H, I = (size_t)s.I, P = T * k;
+  L.nchunks = (int)((T + kChunk - 1) / kChunk);
+  L.max_mtiles = mtile_bound(s, kStreamBM);  // the larger of the two variants' bounds
+  L.z = take(T * E * 4);
+  L.idx = take(P * 4);
+  L.w = take(P * 4);
+  L.chist = take((size_t)L.nchunks * E * 4);
+  L.cbase = take((size_t)L.nchunks * E * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.meta = take(64 * 4);
+  L.tile_e = take((size_t)L.max_mtiles * 4);
+  L.tile_r = take((size_t)L.max_mtiles * 4);
+  L.stok = take(P * 4);
+  L.sw = take(P * 4);
+  L.inv = take(P * 4);
+  if (s.w_fp8) {
+    L.xq = take(T * H);      // e4m3 codes of x, per-token scale
+    L.xs = take(T * 4);
+    L.hamax = take(P * 4);   // running max |h| per sorted row (float bits)
+    L.h = take(P * I * 4);   // fp32 SwiGLU output before quantisation
+    L.hq = take(P * I);      // its e4m3 codes
+    L.hs = take(P * 4);      // per-row scale of the quantised h
+  } else {
+    L.xq = L.xs = L.hamax = L.hq = L.hs = 0;
+    L.h = take(P * I * 2);   // bf16 SwiGLU output
+  }
+  L.y = take(P * H * 2);     // bf16 expert outputs, scaled by rsf * w
+  L.total = off;
+  return L;
+}
+
+}  // namespace beam
+
+using namespace beam;
+
+namespace {
+
+constexpr int kMaxT = 1 << 22;
+
+beam_status check_config(const beam_moe_config* c) {
+  if (!c) return BEAM_ERR_NULL;
+  if (c->n_experts != kExperts) return BEAM_ERR_CONFIG;
+  const int G = c->n_group;
+  if (G < 1 || G > 64 || (G & (G - 1)) != 0) return BEAM_ERR_CONFIG;
+  if (c->topk_group < 1 || c->topk_group > G) return BEAM_ERR_CONFIG;
+  const int gs = kExperts / G;
+  if (c->top_k < 1 || c->top_k > 32 || c->top_k > c->topk_group * gs) return BEAM_ERR_CONFIG;
+  if (!isfinite(c->routed_scaling_factor)) return BEAM_ERR_CONFIG;
+  if (c->x_dtype != BEAM_F32 && c->x_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
+  if (c->w_dtype != BEAM_BF16 && c->w_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
+  if (c->hidden <= 0 || c->hidden % 128 != 0 || c->hidden > 65536) return BEAM_ERR_SHAPE;
+  if (c->intermediate <= 0 || c->intermediate % 128 != 0 || c->intermediate > 65536)
+    return BEAM_ERR_SHAPE;
+  return BEAM_OK;
+}
+
+Shape shape_of(const beam_moe_config* c, int32_t T) {
+  Shape s;
+  s.T = T;
+  s.H = c->hidden;
+  s.I = c->intermediate;
+  s.E = c->n_experts;
+  s.n_group = c->n_group;
+  s.topk_group = c->topk_group;
+  s.top_k = c->top_k;
+  s.rsf = c->routed_scaling_factor;
+  s.x_f32 = c->x_dtype == BEAM_F32;
+  s.w_fp8 = c->w_dtype == BEAM_FP8_E4M3;
+  return s;
+}
+
+bool misaligned(const void* p) { return p && (((uintptr_t)p) & 15u) != 0; }
+
+#define BEAM_LAUNCH(call)                      \
+  do {                                         \
+    if ((call) != hipSuccess) return BEAM_ERR_HIP; \
+  } while (0)
+
+// Routing and permutation shared by route and forward. Fills the sorted
+// arrays when `permute` is set; `BM` is the M-tile height of the expert GEMMs.
+struct Buffers {
+  float* z;
+  int32_t* idx;
+  float* w;
+  int32_t *chist, *cbase, *counts, *offsets, *meta, *tile_e, *tile_r, *stok, *inv;
+  float* sw;
+};
+
+Buffers carve(const Layout& L, void* ws) {
+  uint8_t* b = (uint8_t*)ws;
+  Buffers B;
+  B.z = (float*)(b + L.z);
+  B.idx = (int32_t*)(b + L.idx);
+  B.w = (float*)(b + L.w);
+  B.chist = (int32_t*)(b + L.chist);
+  B.cbase = (int32_t*)(b + L.cbase);
+  B.counts = (int32_t*)(b + L.counts);
+  B.offsets = (int32_t*)(b + L.offsets);
+  B.meta = (int32_t*)(b + L.meta);
+  B.tile_e = (int32_t*)(b + L.tile_e);
+  B.tile_r = (int32_t*)(b + L.tile_r);
+  B.stok = (int32_t*)(b + L.stok);
+  B.sw = (float*)(b + L.sw);
+  B.inv = (int32_t*)(b + L.inv);
+  return B;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t beam_moe_workspace_bytes(const beam_moe_config* cfg, int32_t T) {
+  if (check_config(cfg) != BEAM_OK || T < 0 || T > kMaxT) return 0;
+  return make_layout(shape_of(cfg, T)).total;
+}
+
+const char* beam_moe_status_string(int32_t status) {
+  switch (status) {
+    case BEAM_OK: return "ok";
+    case BEAM_ERR_NULL: return "a required pointer is NULL";
+    case BEAM_ERR_CONFIG: return "routing parameters outside the supported set";
+    case BEAM_ERR_SHAPE: return "token count, hidden or intermediate size outside the supported set";
+    case BEAM_ERR_DTYPE: return "unsupported dtype combination or missing fp8 scales";
+    case BEAM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case BEAM_ERR_WORKSPACE: return "workspace missing or smaller than beam_moe_workspace_bytes()";
+    case BEAM_ERR_HIP: return "the HIP runtime reported an error";
+    default: return "unknown status";
+  }
+}
+
+beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
+                           const float* router_w, const float* expert_bias, int32_t* topk_idx,
+                           float* topk_w, float* router_logits, int32_t* expert_counts,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const beam_status cs = check_config(cfg);
+  if (cs != BEAM_OK) return cs;
+  if (T < 0 || T > kMaxT) return BEAM_ERR_SHAPE;
+  if (T == 0) return BEAM_OK;
+  if (!x || !router_w || !expert_bias || !topk_idx || !topk_w) return BEAM_ERR_NULL;
+  if (!workspace) return BEAM_ERR_WORKSPACE;
+  if (misaligned(x) || misaligned(router_w) || misaligned(expert_bias) || misaligned(topk_idx) ||
+      misaligned(topk_w) || misaligned(router_logits) || misaligned(expert_counts) ||
+      misaligned(workspace))
+    return BEAM_ERR_ALIGN;
+  const Shape s = shape_of(cfg, T);
+  const Layout L = make_layout(s);
+  if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  Buffers B = carve(L, workspace);
+  float* z = router_logits ? router_logits : B.z;
+  BEAM_LAUNCH(launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
+  BEAM_LAUNCH(launch_select(z, expert_bias, T, s.n_group, s.topk_group, s.top_k, topk_idx, topk_w, st));
+  if (expert_counts) {
+    BEAM_LAUNCH(launch_perm_hist(topk_idx, T, s.top_k, B.chist, st));
+    BEAM_LAUNCH(launch_perm_scan(B.chist, L.nchunks, kTiledBM, B.cbase, B.counts, B.offsets,
+                                 B.meta, B.tile_e, B.tile_r, expert_counts, st));
+  }
+  return BEAM_OK;
+}
+
+beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x,
+                             const float* router_w, const float* expert_bias, const void* w_gate,
+                             const void* w_up, const void* w_down, const float* w_gate_scale,
+                             const float* w_up_scale, const float* w_down_scale, void* out,
+                             int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
+                             float* router_logits_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  const beam_status cs = check_config(cfg);
+  if (cs != BEAM_OK) return cs;
+  if (T < 0 || T > kMaxT) return BEAM_ERR_SHAPE;
+  if (T == 0) return BEAM_OK;
+  if (!x || !router_w || !expert_bias || !w_gate || !w_up || !w_down || !out) return BEAM_ERR_NULL;
+  const bool fp8 = cfg->w_dtype == BEAM_FP8_E4M3;
+  if (fp8 && (!w_gate_scale || !w_up_scale || !w_down_scale)) return BEAM_ERR_DTYPE;
+  if (!workspace) return BEAM_ERR_WORKSPACE;
+  if (misaligned(x) || misaligned(router_w) || misaligned(expert_bias) || misaligned(w_gate) ||
+      misaligned(w_up) || misaligned(w_down) || misaligned(out) || misaligned(topk_idx_out) ||
+      misaligned(topk_w_out) || misaligned(expert_counts_out) || misaligned(router_logits_out) ||
+      misaligned(workspace) ||
+      (fp8 && (misaligned(w_gate_scale) || misaligned(w_up_scale) || misaligned(w_down_scale))))
+    return BEAM_ERR_ALIGN;
+  const Shape s = shape_of(cfg, T);
+  const Layout L = make_layout(s);
+  if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  Buffers B = carve(L, workspace);
+  float* z = router_logits_out ? router_logits_out : B.z;
+  int32_t* idx = topk_idx_out ? topk_idx_out : B.idx;
+  float* w = topk_w_out ? topk_w_out : B.w;
+  const int k = s.top_k;
+  const int BM = use_stream_gemm(s) ? kStreamBM : kTiledBM;
+
+  BEAM_LAUNCH(launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
+  BEAM_LAUNCH(launch_select(z, expert_bias, T, s.n_group, s.topk_group, k, idx, w, st));
+  BEAM_LAUNCH(launch_perm_hist(idx, T, k, B.chist, st));
+  BEAM_LAUNCH(launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts, B.offsets, B.meta,
+                               B.tile_e, B.tile_r, expert_counts_out, st));
+  BEAM_LAUNCH(launch_perm_scatter(idx, w, T, k, s.rsf, B.cbase, B.offsets, B.stok, B.sw, B.inv, st));
+
+  GemmArgs g{};
+  g.tile_e = B.tile_e;
+  g.tile_r = B.tile_r;
+  g.meta = B.meta;
+  g.offsets = B.offsets;
+  g.stok = B.stok;
+  g.sw = B.sw;
+  g.max_mtiles = L.max_mtiles;
+  void* y = ws + L.y;
+
+  if (fp8) {
+    uint8_t* xq = ws + L.xq;
+    float* xs = (float*)(ws + L.xs);
+    uint32_t* hamax = (uint32_t*)(ws + L.hamax);
+    float* hf = (float*)(ws + L.h);
+    float* hs = (float*)(ws + L.hs);
+    uint8_t* hq = ws + L.hq;
+    BEAM_LAUNCH(launch_quant_x(x, s.x_f32, T, s.H, k, xq, xs, hamax, st));
+    g.a = xq;
+    g.a_scale = xs;
+    g.w0 = w_gate;
+    g.w1 = w_up;
+    g.ws0 = w_gate_scale;
+    g.ws1 = w_up_scale;
+    g.out = hf;
+    g.hamax = hamax;
+    g.K = s.H;
+    g.N = s.I;
+    BEAM_LAUNCH(launch_gateup(s, g, st));
+    BEAM_LAUNCH(launch_quant_h(hf, hamax, T * k, s.I, hq, hs, st));
+    g.a = hq;
+    g.a_scale = hs;
+    g.w0 = w_down;
+    g.w1 = nullptr;
+    g.ws0 = w_down_scale;
+    g.ws1 = nullptr;
+    g.out = y;
+    g.hamax = nullptr;
+    g.K = s.I;
+    g.N = s.H;
+    BEAM_LAUNCH(launch_down(s, g, st));
+  } else {
+    void* h = ws + L.h;
+    g.a = x;
+    g.w0 = w_gate;
+    g.w1 = w_up;
+    g.out = h;
+    g.K = s.H;
+    g.N = s.I;
+    BEAM_LAUNCH(launch_gateup(s, g, st));
+    g.a = h;
+    g.w0 = w_down;
+    g.w1 = nullptr;
+    g.out = y;
+    g.K = s.I;
+    g.N = s.H;
+    BEAM_LAUNCH(launch_down(s, g, st));
+  }
+  BEAM_LAUNCH(launch_combine(y, B.inv, T, k, s.H, s.x_f32, out, st));
+  return BEAM_OK;
+}
+
+}  // extern "C"

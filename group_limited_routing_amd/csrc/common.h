@@ -1,0 +1,96 @@
+// Shared device helpers for the gfx950 kernels of the Beam MoE block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace beam {
+
+constexpr int kWave = 64;
+constexpr int kExperts = 256;   // the block is built for Beam's 256 experts
+constexpr int kChunk = 256;     // tokens per permutation chunk (one workgroup)
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((__vector_size__(8 * sizeof(int32_t)))) int32_t i32x8;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// 16x16x32 bf16 MFMA, fp32 accumulate. Operand layout (per lane l of 64):
+// A: row l%16, eight k values; B: column l%16, eight k values; the products
+// pair element i of A's lane group l/16 with element i of B's lane group l/16.
+// C: column l%16, rows 4*(l/16) + 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x4 fp32 MFMA: A row l%16 / B column l%16, k slot l/16; C as above.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 16x16x128 fp8 (OCP E4M3 on both operands) MFMA, fp32 accumulate. Each
+// lane holds 32 one-byte values of its row (A) or column (B); the E8M0 block
+// scales are 0x7F = 2^0, so this is the unscaled product.
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+}
+
+// fp32 -> OCP E4M3 code, round to nearest even, finite overflow saturates to
+// +-448, NaN -> 0x7F. Written from the format: bias 7, 3 mantissa bits,
+// subnormal spacing 2^-9, no infinity, largest finite 1.75 * 2^8.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;  // >= 448 (and +-inf): saturate
+  if (a < 0x3c800000u) {                       // below 2^-6: multiples of 2^-9
+    const float q = rintf(__uint_as_float(a) * 512.0f);  // exact scaling, RNE
+    return sign | (uint32_t)q;                  // q == 8 is the code of 2^-6
+  }
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);   // RNE to 3 mantissa bits
+  const uint32_t e = (r >> 23) - 120u;                   // rebias 127 -> 7
+  const uint32_t code = (e << 3) | ((r >> 20) & 7u);
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  return 1.0f / (1.0f + expf(-z));
+}
+
+__device__ __forceinline__ float silu_f32(float v) {
+  return v / (1.0f + expf(-v));
+}
+
+}  // namespace beam

@@ -1,0 +1,656 @@
+// Grouped expert GEMMs of the Beam MoE block on gfx950.
+//
+// Beam launch post ("Introducing Beam"), section "Mixture of Experts": each
+// expert is a SwiGLU MLP with intermediate size 2560; section "Residual
+// Stream": the SwiGLU product is computed in fp32. Expert e computes
+//   h = silu(x W_gate[e]^T) * (x W_up[e]^T)      (gate/up pass, "mode 0")
+//   y = rsf * w * (h W_down[e]^T)                 (down pass, "mode 1")
+// for the rows the permutation sorted into expert e's contiguous range.
+//
+// Both passes walk a device-built list of M-tiles (expert, first row). A
+// workgroup takes one M-tile and one block of output columns; the grid is
+// sized from a T-based bound on the tile count and surplus workgroups exit at
+// once, so the host never reads the counts.
+//
+// Two variants:
+//  * stream (few rows per expert, decode): 16-row M-tiles; every wave owns
+//    its own weight rows and streams them from HBM straight into MFMA
+//    operands through a D-deep register ring, with no LDS and no barriers.
+//    The 16 token rows come from L2.
+//  * tiled (prefill): 128-row M-tiles; the A rows and 128 weight rows are
+//    staged through XOR-swizzled LDS, double buffered, and 4 waves each
+//    compute a 64 x 64 block.
+// In the gate/up pass a wave always holds the gate and the up accumulators
+// of the same output columns, so the SwiGLU epilogue is elementwise.
+//
+// Weights are bf16 (16x16x32 bf16 MFMA) or OCP E4M3 codes with one fp32
+// scale per output row (16x16x128 fp8 MFMA). With fp8 weights the A operand
+// is E4M3 too (x quantised per token, h per row); the scales are applied to
+// the fp32 accumulators in the epilogue, and the gate/up pass writes fp32 h
+// and records each row's max |h| for the quantisation of the down pass.
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+
+// Per-type constants. One MFMA consumes KSTEP values of k; a lane's operand
+// is OPB bytes of one row.
+template <bool FP8>
+struct WTraits;
+template <>
+struct WTraits<false> {
+  using W = uint16_t;
+  static constexpr int KSTEP = 32, OPB = 16;
+};
+template <>
+struct WTraits<true> {
+  using W = uint8_t;
+  static constexpr int KSTEP = 128, OPB = 32;
+};
+
+// A 32-byte operand register (fp8) or a 16-byte one (bf16).
+struct Op32 {
+  u32x4 lo, hi;
+};
+
+__device__ __forceinline__ f32x4 mfma_op(const u32x4& a, const u32x4& b, f32x4 c) {
+  return mfma_bf16(as_bf16x8(a), as_bf16x8(b), c);
+}
+__device__ __forceinline__ f32x4 mfma_op(const Op32& a, const Op32& b, f32x4 c) {
+  i32x8 av, bv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    av[i] = (int)a.lo[i];
+    av[4 + i] = (int)a.hi[i];
+    bv[i] = (int)b.lo[i];
+    bv[4 + i] = (int)b.hi[i];
+  }
+  return mfma_fp8(av, bv, c);
+}
+
+template <bool FP8>
+using OpReg = typename std::conditional<FP8, Op32, u32x4>::type;
+
+template <bool FP8>
+__device__ __forceinline__ OpReg<FP8> load_op(const void* p) {
+  if constexpr (FP8) {
+    Op32 o;
+    o.lo = ld16(p);
+    o.hi = ld16((const uint8_t*)p + 16);
+    return o;
+  } else {
+    return ld16(p);
+  }
+}
+
+// The A operand of a bf16 pass may be stored as fp32 (x in fp32); it is then
+// rounded to bf16 (nearest even) on load. 8 values per lane.
+template <typename AT>
+struct ALoad16;
+template <>
+struct ALoad16<uint16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = ld16(p); }
+  __device__ __forceinline__ u32x4 bits() const { return v; }
+  __device__ __forceinline__ void floats(float* f) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_bits_to_f32(v[i] & 0xffffu);
+      f[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+    }
+  }
+};
+template <>
+struct ALoad16<float> {
+  u32x4 v0, v1;
+  __device__ __forceinline__ void load(const float* p) {
+    v0 = ld16(p);
+    v1 = ld16(p + 4);
+  }
+  __device__ __forceinline__ void floats(float* f) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = __uint_as_float(v0[i]);
+      f[4 + i] = __uint_as_float(v1[i]);
+    }
+  }
+  __device__ __forceinline__ u32x4 bits() const {
+    u32x4 o;
+    o[0] = pack_bf16x2(__uint_as_float(v0[0]), __uint_as_float(v0[1]));
+    o[1] = pack_bf16x2(__uint_as_float(v0[2]), __uint_as_float(v0[3]));
+    o[2] = pack_bf16x2(__uint_as_float(v1[0]), __uint_as_float(v1[1]));
+    o[3] = pack_bf16x2(__uint_as_float(v1[2]), __uint_as_float(v1[3]));
+    return o;
+  }
+};
+
+struct TileInfo {
+  int e, row0, rows;
+};
+
+__device__ __forceinline__ bool tile_info(const GemmArgs& p, int mt, int BM, TileInfo& ti) {
+  if (mt >= p.meta[0]) return false;
+  ti.e = p.tile_e[mt];
+  ti.row0 = p.tile_r[mt];
+  ti.rows = min(BM, p.offsets[ti.e + 1] - ti.row0);
+  return true;
+}
+
+// Epilogue of one 16x16 accumulator pair / block. `row` is the tile-local
+// row, `n` the output column; returns nothing, stores one value.
+template <bool FP8>
+__device__ __forceinline__ float gateup_value(const GemmArgs& p, const TileInfo& ti, int row, int n,
+                                              float gacc, float uacc) {
+  if constexpr (FP8) {
+    const float xs = p.a_scale[p.stok[ti.row0 + row]];
+    const float gv = gacc * xs * p.ws0[(size_t)ti.e * p.N + n];
+    const float uv = uacc * xs * p.ws1[(size_t)ti.e * p.N + n];
+    return silu_f32(gv) * uv;
+  } else {
+    return silu_f32(gacc) * uacc;
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ float down_value(const GemmArgs& p, const TileInfo& ti, int row, int n,
+                                            float acc) {
+  if constexpr (FP8) {
+    return acc * p.a_scale[ti.row0 + row] * p.ws0[(size_t)ti.e * p.N + n] * p.sw[ti.row0 + row];
+  } else {
+    return acc * p.sw[ti.row0 + row];
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void store_h(const GemmArgs& p, size_t off, float h) {
+  if constexpr (FP8)
+    ((float*)p.out)[off] = h;
+  else
+    ((uint16_t*)p.out)[off] = (uint16_t)f32_to_bf16_bits(h);
+}
+
+// Row-wise max |h| over the 16 columns a lane group holds, then one atomicMax
+// per row. |h| >= 0, so its float bits order like unsigned integers; the
+// maximum does not depend on the order of the updates.
+__device__ __forceinline__ void row_amax_update(uint32_t* hamax, int grow, float v, bool valid) {
+  float m = fabsf(v);
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (valid && (threadIdx.x & 15) == 0) atomicMax(&hamax[grow], __float_as_uint(m));
+}
+
+// ---------------------------------------------------------------- stream variant
+// FN = 16-row weight fragments per wave (mode 0: FN/2 gate + FN/2 up),
+// D = depth of the register prefetch ring (in MFMA k-steps).
+template <int MODE, typename AT, bool FP8, int FN, int D>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
+  using WT = typename WTraits<FP8>::W;
+  constexpr int KSTEP = WTraits<FP8>::KSTEP;
+  constexpr int LANE_K = KSTEP / 4;  // k values per lane per step
+  constexpr int HALF = FN / 2;
+  constexpr int COLS_W = (MODE == 0) ? 16 * HALF : 16 * FN;  // output columns per wave
+  constexpr int COLS = 4 * COLS_W;                           // per workgroup
+  const int ntn = p.N / COLS;
+  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  TileInfo ti;
+  if (!tile_info(p, mt, kStreamBM, ti)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N;
+
+  // Padded rows (r >= rows) repeat the last real row; their results are not stored.
+  const int ar = min(r, ti.rows - 1);
+  const AT* arow = (MODE == 0) ? (const AT*)p.a + (size_t)p.stok[ti.row0 + ar] * K + LANE_K * g
+                               : (const AT*)p.a + (size_t)(ti.row0 + ar) * K + LANE_K * g;
+  const int ncol0 = nt * COLS + wave * COLS_W;
+  const WT* brow[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    int n;
+    const WT* W;
+    if (MODE == 0) {
+      n = ncol0 + (f % HALF) * 16 + r;
+      W = (const WT*)(f < HALF ? p.w0 : p.w1);
+    } else {
+      n = ncol0 + f * 16 + r;
+      W = (const WT*)p.w0;
+    }
+    brow[f] = W + ((size_t)ti.e * N + n) * K + LANE_K * g;
+  }
+
+  f32x4 acc[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = K / KSTEP;  // K is a multiple of 128: bf16 nks % 4 == 0, fp8 nks >= 1
+  using OR = OpReg<FP8>;
+  OR bq[D][FN];
+  OR aq8[FP8 ? D : 1];
+  using AL16 = typename std::conditional<FP8, ALoad16<uint16_t>, ALoad16<AT>>::type;
+  AL16 aq16[FP8 ? 1 : D];
+  auto load_step = [&](int d, int s) {
+    if constexpr (FP8)
+      aq8[d] = load_op<true>(arow + (size_t)s * KSTEP);
+    else
+      aq16[d].load((const typename std::conditional<FP8, uint16_t, AT>::type*)arow + (size_t)s * KSTEP);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) bq[d][f] = load_op<FP8>(brow[f] + (size_t)s * KSTEP);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nks) load_step(d, d);
+  for (int s0 = 0; s0 < nks; s0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (s0 + d < nks) {
+        OR a;
+        if constexpr (FP8)
+          a = aq8[d];
+        else
+          a = aq16[d].bits();
+#pragma unroll
+        for (int f = 0; f < FN; ++f) acc[f] = mfma_op(a, bq[d][f], acc[f]);
+        const int sn = s0 + d + D;
+        if (sn < nks) load_step(d, sn);
+      }
+    }
+  }
+
+  if (MODE == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g + i;
+      const bool valid = row < ti.rows;
+      float rowmax = 0.f;
+#pragma unroll
+      for (int f = 0; f < HALF; ++f) {
+        const int n = ncol0 + f * 16 + r;
+        if (valid) {
+          const float h = gateup_value<FP8>(p, ti, row, n, acc[f][i], acc[f + HALF][i]);
+          store_h<FP8>(p, (size_t)(ti.row0 + row) * N + n, h);
+          rowmax = fmaxf(rowmax, fabsf(h));
+        }
+      }
+      if constexpr (FP8) row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
+    }
+  } else {
+    uint16_t* out = (uint16_t*)p.out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g + i;
+      if (row < ti.rows) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int n = ncol0 + f * 16 + r;
+          out[(size_t)(ti.row0 + row) * N + n] =
+              (uint16_t)f32_to_bf16_bits(down_value<FP8>(p, ti, row, n, acc[f][i]));
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- tiled variant
+// An LDS tile row holds 128 bytes of k (64 bf16 or 128 fp8 values) as eight
+// 16-byte chunks; chunk c of row r lives at chunk position c ^ (r & 7), so the
+// 16 rows of one MFMA operand read spread over all banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+template <int MODE, typename AT, bool FP8>
+__global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
+  using WT = typename WTraits<FP8>::W;
+  constexpr int BM = kTiledBM, NBR = 128;
+  constexpr int BK = FP8 ? 128 : 64;           // k values per stage (128 bytes per row)
+  constexpr int A_BYTES = BM * 128, B_BYTES = NBR * 128, STAGE = A_BYTES + B_BYTES;
+  constexpr int COLS = (MODE == 0) ? 64 : 128;  // output columns per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int ntn = p.N / COLS;
+  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  TileInfo ti;
+  if (!tile_info(p, mt, BM, ti)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1, r = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N;
+  const int n0 = nt * COLS;
+  constexpr int CH = BK / 8;  // values per 16-byte LDS chunk of A: bf16 8, fp8 16
+
+  // Global -> LDS assignment: 1024 chunks of A and of B per stage, 4 each per thread.
+  const AT* agp[4];
+  const WT* bgp[4];
+  int soff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + 256 * i, lr = q >> 3, c = q & 7;
+    const int ar = min(lr, ti.rows - 1);
+    agp[i] = (MODE == 0) ? (const AT*)p.a + (size_t)p.stok[ti.row0 + ar] * K + c * CH
+                         : (const AT*)p.a + (size_t)(ti.row0 + ar) * K + c * CH;
+    const WT* W;
+    int n;
+    if (MODE == 0) {
+      W = (const WT*)(lr < 64 ? p.w0 : p.w1);
+      n = n0 + (lr & 63);
+    } else {
+      W = (const WT*)p.w0;
+      n = n0 + lr;
+    }
+    bgp[i] = W + ((size_t)ti.e * N + n) * K + c * CH;
+    soff[i] = swz(lr, c);
+  }
+
+  int arow_l[4], brow_l[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    arow_l[f] = wm * 64 + f * 16 + r;
+    brow_l[f] = (MODE == 0) ? ((f < 2) ? wn * 32 + f * 16 + r : 64 + wn * 32 + (f - 2) * 16 + r)
+                            : wn * 64 + f * 16 + r;
+  }
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  using AL = typename std::conditional<FP8, ALoad16<uint16_t>, ALoad16<AT>>::type;
+  AL ra[4];
+  u32x4 rb[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (FP8)
+        ra[i].v = ld16(agp[i] + (size_t)kt * BK);
+      else
+        ra[i].load(agp[i] + (size_t)kt * BK);
+      rb[i] = ld16(bgp[i] + (size_t)kt * BK);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* base = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st16(base + soff[i], ra[i].bits());
+      st16(base + A_BYTES + soff[i], rb[i]);
+    }
+  };
+
+  const int nk = K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint8_t* As = smem + buf * STAGE;
+    const uint8_t* Bs = As + A_BYTES;
+    if constexpr (FP8) {
+      // one 16x16x128 MFMA per stage: lane group g holds chunks 2g and 2g+1
+      Op32 af[4], bfr[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        af[f].lo = ld16(As + swz(arow_l[f], 2 * g));
+        af[f].hi = ld16(As + swz(arow_l[f], 2 * g + 1));
+        bfr[f].lo = ld16(Bs + swz(brow_l[f], 2 * g));
+        bfr[f].hi = ld16(Bs + swz(brow_l[f], 2 * g + 1));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op(af[i], bfr[j], acc[i][j]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 af[4], bfr[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          af[f] = ld16(As + swz(arow_l[f], s * 4 + g));
+          bfr[f] = ld16(Bs + swz(brow_l[f], s * 4 + g));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_op(af[i], bfr[j], acc[i][j]);
+      }
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (MODE == 0) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 64 + fm * 16 + 4 * g + i;
+        const bool valid = row < ti.rows;
+        float rowmax = 0.f;
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+          const int n = n0 + wn * 32 + fn * 16 + r;
+          if (valid) {
+            const float h = gateup_value<FP8>(p, ti, row, n, acc[fm][fn][i], acc[fm][fn + 2][i]);
+            store_h<FP8>(p, (size_t)(ti.row0 + row) * N + n, h);
+            rowmax = fmaxf(rowmax, fabsf(h));
+          }
+        }
+        if constexpr (FP8) row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
+      }
+  } else {
+    uint16_t* out = (uint16_t*)p.out;
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 64 + fm * 16 + 4 * g + i;
+        if (row < ti.rows) {
+#pragma unroll
+          for (int fn = 0; fn < 4; ++fn) {
+            const int n = n0 + wn * 64 + fn * 16 + r;
+            out[(size_t)(ti.row0 + row) * N + n] =
+                (uint16_t)f32_to_bf16_bits(down_value<FP8>(p, ti, row, n, acc[fm][fn][i]));
+          }
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+int mtile_bound(const Shape& s, int BM) {
+  const long long pairs = (long long)s.T * s.top_k;
+  const long long active = pairs < s.E ? pairs : s.E;
+  return (int)(active + pairs / BM + 1);
+}
+
+bool use_stream_gemm(const Shape& s) {
+  // Up to about 16 rows per expert on average the weights are streamed once
+  // per 16-row tile; beyond that the LDS-tiled variant reuses them better.
+  return (long long)s.T * s.top_k <= 16LL * s.E;
+}
+
+template <int MODE, typename AT, bool FP8>
+static void launch_stream(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  constexpr int D = FP8 ? 2 : 4;
+  if (MODE == 0) {
+    dim3 grid(mtile_bound(s, kStreamBM) * (g.N / 128));
+    gemm_stream_kernel<0, AT, FP8, 4, D><<<grid, 256, 0, st>>>(g);
+  } else if (g.N % 256 == 0) {
+    dim3 grid(mtile_bound(s, kStreamBM) * (g.N / 256));
+    gemm_stream_kernel<1, AT, FP8, 4, D><<<grid, 256, 0, st>>>(g);
+  } else {
+    dim3 grid(mtile_bound(s, kStreamBM) * (g.N / 128));
+    gemm_stream_kernel<1, AT, FP8, 2, D><<<grid, 256, 0, st>>>(g);
+  }
+}
+
+template <int MODE, typename AT, bool FP8>
+static void launch_tiled(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  dim3 grid(mtile_bound(s, kTiledBM) * (g.N / (MODE == 0 ? 64 : 128)));
+  gemm_tiled_kernel<MODE, AT, FP8><<<grid, 256, 0, st>>>(g);
+}
+
+hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  const bool stream = use_stream_gemm(s);
+  if (s.w_fp8) {
+    if (stream)
+      launch_stream<0, uint8_t, true>(s, g, st);
+    else
+      launch_tiled<0, uint8_t, true>(s, g, st);
+  } else if (s.x_f32) {
+    if (stream)
+      launch_stream<0, float, false>(s, g, st);
+    else
+      launch_tiled<0, float, false>(s, g, st);
+  } else {
+    if (stream)
+      launch_stream<0, uint16_t, false>(s, g, st);
+    else
+      launch_tiled<0, uint16_t, false>(s, g, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  const bool stream = use_stream_gemm(s);
+  if (s.w_fp8) {
+    if (stream)
+      launch_stream<1, uint8_t, true>(s, g, st);
+    else
+      launch_tiled<1, uint8_t, true>(s, g, st);
+  } else {
+    if (stream)
+      launch_stream<1, uint16_t, false>(s, g, st);
+    else
+      launch_tiled<1, uint16_t, false>(s, g, st);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- combine
+// out[t] = sum over slots j (ascending) of y_perm[inv[t, j]], in fp32; the
+// rows already carry rsf * w. One thread per 8 output values.
+template <int OUT_F32>
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ inv, int T,
+                                                      int k, int H, void* __restrict__ out) {
+  const int vpr = H / 8;
+  const long long v = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (v >= (long long)T * vpr) return;
+  const int t = (int)(v / vpr), c = (int)(v % vpr);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int pos = inv[(size_t)t * k + j];
+    const u32x4 q = ld16(y + (size_t)pos * H + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_bits_to_f32(q[i] & 0xffffu);
+      acc[2 * i + 1] += bf16_bits_to_f32(q[i] >> 16);
+    }
+  }
+  if (OUT_F32) {
+    float* o = (float*)out + (size_t)t * H + c * 8;
+    st16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                  __float_as_uint(acc[3])});
+    st16(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]),
+                      __float_as_uint(acc[7])});
+  } else {
+    uint16_t* o = (uint16_t*)out + (size_t)t * H + c * 8;
+    st16(o, u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                  pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])});
+  }
+}
+
+hipError_t launch_combine(const void* y, const int32_t* inv, int T, int k, int H, int out_f32,
+                          void* out, hipStream_t st) {
+  const long long n = (long long)T * (H / 8);
+  const int blocks = (int)((n + 255) / 256);
+  if (out_f32)
+    combine_kernel<1><<<blocks, 256, 0, st>>>((const uint16_t*)y, inv, T, k, H, out);
+  else
+    combine_kernel<0><<<blocks, 256, 0, st>>>((const uint16_t*)y, inv, T, k, H, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fp8 quantisation
+// Per-row E4M3 quantisation: amax = max |v|; scale = amax / 448 (1 if amax is
+// 0); code = e4m3(v * (448 / amax)), all correctly rounded fp32 operations.
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// One workgroup per token; also clears the token's top_k entries of the
+// running |h| maxima used by the gate/up pass (rows t*k .. t*k+k-1 of the
+// sorted order: together the T workgroups clear all T*k rows).
+template <typename XT>
+__global__ __launch_bounds__(256) void quant_x_kernel(const XT* __restrict__ x, int H,
+                                                      uint8_t* __restrict__ xq,
+                                                      float* __restrict__ xs,
+                                                      uint32_t* __restrict__ hamax, int k) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const XT* row = x + (size_t)t * H;
+  float m = 0.f;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    ALoad16<XT> v;
+    v.load(row + c);
+    float f[8];
+    v.floats(f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  }
+  const float amax = block_max(m, red);
+  const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    ALoad16<XT> v;
+    v.load(row + c);
+    float f[8];
+    v.floats(f);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i >> 2] |= f32_to_e4m3(f[i] * inv) << (8 * (i & 3));
+    *reinterpret_cast<u32x2*>(xq + (size_t)t * H + c) = u32x2{w[0], w[1]};
+  }
+  if (threadIdx.x == 0) xs[t] = amax > 0.f ? amax / 448.0f : 1.0f;
+  if (threadIdx.x < k) hamax[(size_t)t * k + threadIdx.x] = 0u;
+}
+
+// One workgroup per sorted row of h.
+__global__ __launch_bounds__(256) void quant_h_kernel(const float* __restrict__ hf,
+                                                      const uint32_t* __restrict__ hamax, int I,
+                                                      uint8_t* __restrict__ hq,
+                                                      float* __restrict__ hs) {
+  const size_t row = blockIdx.x;
+  const float amax = __uint_as_float(hamax[row]);
+  const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+  for (int c = threadIdx.x * 4; c < I; c += 256 * 4) {
+    const u32x4 v = ld16(hf + row * I + c);
+    uint32_t w = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= f32_to_e4m3(__uint_as_float(v[i]) * inv) << (8 * i);
+    *reinterpret_cast<uint32_t*>(hq + row * I + c) = w;
+  }
+  if (threadIdx.x == 0) hs[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+}
+
+hipError_t launch_quant_x(const void* x, int x_f32, int T, int H, int k, uint8_t* xq, float* xs,
+                          uint32_t* hamax, hipStream_t st) {
+  if (x_f32)
+    quant_x_kernel<float><<<T, 256, 0, st>>>((const float*)x, H, xq, xs, hamax, k);
+  else
+    quant_x_kernel<uint16_t><<<T, 256, 0, st>>>((const uint16_t*)x, H, xq, xs, hamax, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_h(const float* hf, const uint32_t* hamax, int rows, int I, uint8_t* hq,
+                          float* hs, hipStream_t st) {
+  quant_h_kernel<<<rows, 256, 0, st>>>(hf, hamax, I, hq, hs);
+  return hipGetLastError();
+}
+
+}  // namespace beam

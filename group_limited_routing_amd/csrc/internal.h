@@ -1,0 +1,72 @@
+// Internal launchers and workspace layout of the Beam MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace beam {
+
+// Row tile (tokens per M-tile) of the two expert-GEMM variants.
+constexpr int kStreamBM = 16;   // decode: weight streaming, one MFMA row block
+constexpr int kTiledBM = 128;   // prefill: LDS-staged MFMA tiles
+
+struct Shape {
+  int T, H, I, E, n_group, topk_group, top_k;
+  float rsf;
+  int x_f32;   // 1: x/out fp32, 0: bf16
+  int w_fp8;   // 1: fp8 e4m3 weights with per-row scales
+};
+
+// Byte offsets of each workspace region (all 256-byte aligned).
+struct Layout {
+  size_t z, idx, w, chist, cbase, counts, offsets, meta, tile_e, tile_r;
+  size_t stok, sw, inv, xq, xs, hamax, h, hq, hs, y, total;
+  int nchunks, max_mtiles;
+};
+
+Layout make_layout(const Shape& s);
+bool use_stream_gemm(const Shape& s);
+int mtile_bound(const Shape& s, int BM);
+
+hipError_t launch_router_logits(const void* x, int x_f32, const float* W, float* z, int T, int H,
+                                hipStream_t st);
+hipError_t launch_select(const float* z, const float* bias, int T, int n_group, int topk_group,
+                         int top_k, int32_t* idx, float* w, hipStream_t st);
+hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int32_t* chist, hipStream_t st);
+hipError_t launch_perm_scan(const int32_t* chist, int nchunks, int BM, int32_t* cbase,
+                            int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,
+                            int32_t* tile_r, int32_t* counts_out, hipStream_t st);
+hipError_t launch_perm_scatter(const int32_t* idx, const float* w, int T, int k, float rsf,
+                               const int32_t* cbase, const int32_t* offsets, int32_t* stok,
+                               float* sw, int32_t* inv, hipStream_t st);
+
+struct GemmArgs {
+  const void* a;            // gate/up: x [T, H]; down: h_perm [T*k, I]
+  const void* w0;           // gate/up: w_gate; down: w_down
+  const void* w1;           // gate/up: w_up; down: unused
+  const float* ws0;         // fp8 per-row weight scales matching w0 (or null)
+  const float* ws1;         // fp8 per-row weight scales matching w1 (or null)
+  const float* a_scale;     // fp8: per-row activation scales (x: [T], h: [T*k])
+  const int32_t* tile_e;
+  const int32_t* tile_r;
+  const int32_t* meta;
+  const int32_t* offsets;
+  const int32_t* stok;
+  const float* sw;          // rsf * routing weight per sorted row
+  void* out;                // gate/up: h_perm; down: y_perm
+  uint32_t* hamax;          // fp8 gate/up: per-row running max |h| (float bits)
+  int K, N;                 // reduction length and output width
+  int max_mtiles;
+};
+
+hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st);
+hipError_t launch_down(const Shape& s, const GemmArgs& g, hipStream_t st);
+hipError_t launch_combine(const void* y, const int32_t* inv, int T, int k, int H, int out_f32,
+                          void* out, hipStream_t st);
+hipError_t launch_quant_x(const void* x, int x_f32, int T, int H, int k, uint8_t* xq, float* xs,
+                          uint32_t* hamax, hipStream_t st);
+hipError_t launch_quant_h(const float* hf, const uint32_t* hamax, int rows, int I, uint8_t* hq,
+                          float* hs, hipStream_t st);
+
+}  // namespace beam

@@ -1,0 +1,148 @@
+// Token permutation of the Beam MoE block on gfx950: the (token, slot) pairs
+// chosen by the router are ordered by expert, stably by token, so that each
+// expert's rows are contiguous for the grouped expert GEMMs.
+//
+// Tokens are processed in chunks of 256 (one workgroup). Inside a chunk a
+// 256-bit LDS mask per expert records which tokens chose it; a token never
+// chooses the same expert twice, so a pair's rank among the chunk's pairs of
+// the same expert is the number of set mask bits below its token. Per-chunk
+// counts are scanned per expert across chunks, and the per-expert totals are
+// scanned across experts, all with integer arithmetic: the permutation is
+// deterministic and stable (ascending token within each expert).
+#include "common.h"
+#include "internal.h"
+
+namespace beam {
+
+constexpr int kMaskWords = kChunk / 32;  // 8 words of 32 tokens per expert
+
+__device__ __forceinline__ void build_masks(uint32_t* mask, const int32_t* __restrict__ idx, int T,
+                                            int k, int chunk) {
+  for (int i = threadIdx.x; i < kExperts * kMaskWords; i += 256) mask[i] = 0u;
+  __syncthreads();
+  const int t = chunk * kChunk + threadIdx.x;
+  if (t < T) {
+    const uint32_t bit = 1u << (threadIdx.x & 31);
+    const int word = threadIdx.x >> 5;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j];
+      atomicOr(&mask[e * kMaskWords + word], bit);
+    }
+  }
+  __syncthreads();
+}
+
+// chist[c, e] = number of tokens of chunk c that chose expert e.
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                        int32_t* __restrict__ chist) {
+  __shared__ uint32_t mask[kExperts * kMaskWords];
+  build_masks(mask, idx, T, k, blockIdx.x);
+  const int e = threadIdx.x;
+  int cnt = 0;
+#pragma unroll
+  for (int w = 0; w < kMaskWords; ++w) cnt += __popc(mask[e * kMaskWords + w]);
+  chist[(size_t)blockIdx.x * kExperts + e] = cnt;
+}
+
+// Exclusive prefix sum over the 256 threads of the block.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  return base + incl - v;
+}
+
+// One workgroup, thread e = expert e:
+//   cbase[c, e]  = tokens of expert e in chunks before c;
+//   counts[e]    = tokens of expert e; offsets = exclusive scan of counts;
+//   M-tiles of BM rows per expert, listed expert by expert:
+//   tile_e[m] = expert, tile_r[m] = first sorted row; meta[0] = tile count.
+__global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restrict__ chist,
+                                                        int nchunks, int BM,
+                                                        int32_t* __restrict__ cbase,
+                                                        int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ meta,
+                                                        int32_t* __restrict__ tile_e,
+                                                        int32_t* __restrict__ tile_r,
+                                                        int32_t* __restrict__ counts_out) {
+  __shared__ int wsum[4];
+  const int e = threadIdx.x;
+  int run = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    const int h = chist[(size_t)c * kExperts + e];
+    cbase[(size_t)c * kExperts + e] = run;
+    run += h;
+  }
+  counts[e] = run;
+  if (counts_out) counts_out[e] = run;
+  const int off = block_exclusive_scan(run, wsum);
+  offsets[e] = off;
+  if (e == kExperts - 1) offsets[kExperts] = off + run;
+  const int mt = (run + BM - 1) / BM;
+  const int ts = block_exclusive_scan(mt, wsum);
+  for (int i = 0; i < mt; ++i) {
+    tile_e[ts + i] = e;
+    tile_r[ts + i] = off + i * BM;
+  }
+  if (e == kExperts - 1) meta[0] = ts + mt;
+}
+
+// Position of every (token, slot) pair in expert order:
+//   pos = offsets[e] + cbase[chunk, e] + (tokens of the chunk below t that chose e).
+//   stok[pos] = t, sw[pos] = rsf * w[t, slot], inv[t, slot] = pos.
+__global__ __launch_bounds__(256) void perm_scatter_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ w, int T, int k, float rsf,
+    const int32_t* __restrict__ cbase, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ stok, float* __restrict__ sw, int32_t* __restrict__ inv) {
+  __shared__ uint32_t mask[kExperts * kMaskWords];
+  const int c = blockIdx.x;
+  build_masks(mask, idx, T, k, c);
+  const int t = c * kChunk + threadIdx.x;
+  if (t >= T) return;
+  const int word = threadIdx.x >> 5;
+  const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
+  for (int j = 0; j < k; ++j) {
+    const size_t q = (size_t)t * k + j;
+    const int e = idx[q];
+    int rank = cbase[(size_t)c * kExperts + e];
+    for (int ww = 0; ww < word; ++ww) rank += __popc(mask[e * kMaskWords + ww]);
+    rank += __popc(mask[e * kMaskWords + word] & below);
+    const int pos = offsets[e] + rank;
+    stok[pos] = t;
+    sw[pos] = rsf * w[q];
+    inv[q] = pos;
+  }
+}
+
+hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int32_t* chist, hipStream_t st) {
+  perm_hist_kernel<<<(T + kChunk - 1) / kChunk, 256, 0, st>>>(idx, T, k, chist);
+  return hipGetLastError();
+}
+
+hipError_t launch_perm_scan(const int32_t* chist, int nchunks, int BM, int32_t* cbase,
+                            int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,
+                            int32_t* tile_r, int32_t* counts_out, hipStream_t st) {
+  perm_scan_kernel<<<1, 256, 0, st>>>(chist, nchunks, BM, cbase, counts, offsets, meta, tile_e,
+                                      tile_r, counts_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_perm_scatter(const int32_t* idx, const float* w, int T, int k, float rsf,
+                               const int32_t* cbase, const int32_t* offsets, int32_t* stok,
+                               float* sw, int32_t* inv, hipStream_t st) {
+  perm_scatter_kernel<<<(T + kChunk - 1) / kChunk, 256, 0, st>>>(idx, w, T, k, rsf, cbase,
+                                                                  offsets, stok, sw, inv);
+  return hipGetLastError();
+}
+
+}  // namespace beam

@@ -1,0 +1,132 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments before any HIP call (so these run with
+no GPU). Fake, never-dereferenced pointer values stand in for device memory.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "beam_moe.h")
+
+gl = pytest.importorskip("group_limited_routing_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gl.LIB_PATH):
+        pytest.skip("libbeam_moe.so not built")
+    return gl.lib()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(beam_moe_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert declared == sorted(gl.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in range(8):
+        txt = gl.status_string(s)
+        assert txt and txt != "unknown status"
+    assert gl.status_string(99) == "unknown status"
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def _fwd(L, cfg, T, ptrs=None, ws_bytes=1 << 40, **over):
+    p = dict(x=FAKE, rw=FAKE, b=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, sg=None, su=None, sd=None,
+             out=FAKE, idx=None, w=None, cnt=None, logits=None, ws=FAKE)
+    p.update(over)
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.beam_moe_forward(ctypes.byref(cfg) if cfg is not None else None, T, v(p["x"]),
+                              v(p["rw"]), v(p["b"]), v(p["wg"]), v(p["wu"]), v(p["wd"]),
+                              v(p["sg"]), v(p["su"]), v(p["sd"]), v(p["out"]), v(p["idx"]),
+                              v(p["w"]), v(p["cnt"]), v(p["logits"]), v(p["ws"]), ws_bytes, None)
+
+
+def _route(L, cfg, T, ws_bytes=1 << 40, **over):
+    p = dict(x=FAKE, rw=FAKE, b=FAKE, idx=FAKE, w=FAKE, logits=None, cnt=None, ws=FAKE)
+    p.update(over)
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.beam_moe_route(ctypes.byref(cfg), T, v(p["x"]), v(p["rw"]), v(p["b"]), v(p["idx"]),
+                            v(p["w"]), v(p["logits"]), v(p["cnt"]), v(p["ws"]), ws_bytes, None)
+
+
+def beam_cfg(**kw):
+    c = gl.make_config(5120, 2560)
+    for k, val in kw.items():
+        setattr(c, k, val)
+    return c
+
+
+def test_config_checks(L):
+    bad = [dict(n_experts=128), dict(n_group=3), dict(n_group=128), dict(n_group=0),
+           dict(topk_group=0), dict(topk_group=9), dict(top_k=0), dict(top_k=33),
+           dict(n_group=64, topk_group=1, top_k=5), dict(routed_scaling_factor=float("inf"))]
+    for kw in bad:
+        assert _fwd(L, beam_cfg(**kw), 8) == gl.BEAM_ERR_CONFIG, kw
+        assert _route(L, beam_cfg(**kw), 8) == gl.BEAM_ERR_CONFIG, kw
+    for kw in [dict(x_dtype=2), dict(x_dtype=7), dict(w_dtype=0)]:
+        assert _fwd(L, beam_cfg(**kw), 8) == gl.BEAM_ERR_DTYPE, kw
+    for kw in [dict(hidden=5000), dict(hidden=0), dict(intermediate=100), dict(hidden=65536 + 128)]:
+        assert _fwd(L, beam_cfg(**kw), 8) == gl.BEAM_ERR_SHAPE, kw
+    assert _fwd(L, None, 8) == gl.BEAM_ERR_NULL
+
+
+def test_token_count_checks(L):
+    c = beam_cfg()
+    assert _fwd(L, c, -1) == gl.BEAM_ERR_SHAPE
+    assert _fwd(L, c, (1 << 22) + 1) == gl.BEAM_ERR_SHAPE
+    # T == 0 is a no-op that does not look at the pointers
+    assert _fwd(L, c, 0, x=None, out=None, ws=None) == gl.BEAM_OK
+    assert _route(L, c, 0, x=None, idx=None, w=None, ws=None) == gl.BEAM_OK
+
+
+def test_pointer_checks(L):
+    c = beam_cfg()
+    for name in ["x", "rw", "b", "wg", "wu", "wd", "out"]:
+        assert _fwd(L, c, 8, **{name: None}) == gl.BEAM_ERR_NULL, name
+    for name in ["x", "rw", "b", "idx", "w"]:
+        assert _route(L, c, 8, **{name: None}) == gl.BEAM_ERR_NULL, name
+    assert _fwd(L, c, 8, ws=None) == gl.BEAM_ERR_WORKSPACE
+    for name in ["x", "rw", "b", "wg", "wu", "wd", "out", "idx", "w", "cnt", "logits", "ws"]:
+        assert _fwd(L, c, 8, **{name: FAKE + 4}) == gl.BEAM_ERR_ALIGN, name
+    for name in ["x", "rw", "b", "idx", "w", "cnt", "logits", "ws"]:
+        assert _route(L, c, 8, **{name: FAKE + 8}) == gl.BEAM_ERR_ALIGN, name
+
+
+def test_fp8_needs_scales(L):
+    c = beam_cfg(w_dtype=gl.BEAM_FP8_E4M3)
+    assert _fwd(L, c, 8) == gl.BEAM_ERR_DTYPE
+    assert _fwd(L, c, 8, sg=FAKE, su=FAKE) == gl.BEAM_ERR_DTYPE
+    assert _fwd(L, c, 8, sg=FAKE, su=FAKE, sd=FAKE + 4) == gl.BEAM_ERR_ALIGN
+
+
+def test_workspace_size(L):
+    c = beam_cfg()
+    need = gl.workspace_bytes(c, 64)
+    assert need > 0
+    assert _fwd(L, c, 64, ws_bytes=need - 1) == gl.BEAM_ERR_WORKSPACE
+    assert _route(L, c, 64, ws_bytes=need - 1) == gl.BEAM_ERR_WORKSPACE
+    # grows with T; the bf16 SwiGLU and expert-output buffers dominate at large T
+    sizes = [gl.workspace_bytes(c, T) for T in (1, 64, 4096, 16384)]
+    assert sizes == sorted(sizes)
+    T = 16384
+    assert sizes[-1] >= T * 8 * (2560 + 5120) * 2
+    assert sizes[-1] < T * 8 * (2560 + 5120) * 2 * 1.1
+    assert gl.workspace_bytes(c, -1) == 0
+    assert gl.workspace_bytes(beam_cfg(n_group=3), 64) == 0
+    f8 = gl.workspace_bytes(beam_cfg(w_dtype=gl.BEAM_FP8_E4M3), 64)
+    assert f8 > 0

@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Small shapes are compared on every token; they span several M-tiles and
+column tiles and have ragged tails (T, rows per expert and tiles not
+multiples of the tile sizes), and they exercise both expert-GEMM variants
+(weight streaming for few rows per expert, LDS tiles for many) and both
+weight formats. The named Beam workloads (decode T=64, prefill T=4096,
+skewed T=16384, fp8 T=8192) run at full size in the same launch
+configuration the benchmark times: routing is compared on every token and
+the outputs on sampled tokens, which the oracle computes one expert at a
+time.
+"""
+
+import json
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import group_limited_routing_amd as gl
+from parity import (check_logits, check_outputs, check_routing, oracle_reference, run_forward,
+                    output_errors)
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _case(T, H, I, x_dtype="bf16", w_dtype="bf16", bias="normal", seed=0, **routing):
+    cfg = dict(workloads.BEAM)
+    cfg.update(T=T, hidden=H, intermediate=I, x_dtype=x_dtype, w_dtype=w_dtype, bias=bias)
+    cfg.update(routing)
+    return cfg
+
+
+def _inputs(cfg, seed, dev, experts=None):
+    x, rw, b = workloads.make_small_inputs(cfg, seed)
+    w = workloads.make_expert_weights(cfg, seed, dev, experts=experts)
+    return x.to(dev), rw.to(dev), b.to(dev), w
+
+
+def _report(name, rep):
+    print(f"\n[parity] {name}: " + json.dumps(rep), flush=True)
+
+
+def _full_compare(name, cfg, seed=0):
+    """Every token against the oracle."""
+    dev = _dev()
+    x, rw, b, w = _inputs(cfg, seed, dev)
+    out, r = run_forward(x, rw, b, w, cfg)
+    x64 = x.cpu().double().numpy()
+    rw64 = rw.cpu().double().numpy()
+    ora = oracle.route(x64, rw64, b.cpu().double().numpy(), cfg["n_group"], cfg["topk_group"],
+                       cfg["top_k"])
+    rep = {"T": cfg["T"], "H": cfg["hidden"], "I": cfg["intermediate"]}
+    near = check_routing(r, ora, cfg, rep)
+    check_logits(r["router_logits"], x64, rw64, ora["z"])
+    tokens = np.arange(cfg["T"])
+    ref = oracle_reference(tokens, x, rw, b, w, cfg, r["topk_idx"].cpu().numpy(), near)
+    check_outputs(out.cpu().double().numpy(), ref, rep)
+    _report(name, rep)
+    return out, r
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_tiny_workload(seed):
+    """T=128, H=256, I=128, x and out fp32, bf16 experts."""
+    cfg = workloads.workload("tiny")
+    _full_compare(f"tiny seed {seed}", cfg, seed)
+
+
+def test_ragged_stream_variant():
+    cfg = _case(300, 384, 256)          # 2400 pairs: streaming GEMMs; H % 256 != 0
+    _full_compare("ragged stream", cfg, 3)
+
+
+def test_ragged_tiled_variant():
+    cfg = _case(1000, 512, 384)         # 8000 pairs: LDS-tiled GEMMs, ragged tiles
+    _full_compare("ragged tiled", cfg, 4)
+
+
+def test_fp32_x_tiled_variant():
+    cfg = _case(700, 256, 128, x_dtype="f32")
+    _full_compare("fp32 x tiled", cfg, 5)
+
+
+def test_fp8_stream_variant():
+    cfg = _case(200, 512, 256, w_dtype="fp8")
+    _full_compare("fp8 stream", cfg, 6)
+
+
+def test_fp8_tiled_variant():
+    cfg = _case(900, 384, 256, w_dtype="fp8")
+    _full_compare("fp8 tiled", cfg, 7)
+
+
+@pytest.mark.parametrize("n_group,topk_group,top_k", [(1, 1, 8), (8, 8, 8), (64, 16, 8), (8, 4, 1),
+                                                      (16, 3, 12), (4, 2, 32)])
+def test_group_parameters(n_group, topk_group, top_k):
+    cfg = _case(260, 256, 128, n_group=n_group, topk_group=topk_group, top_k=top_k)
+    _full_compare(f"groups {n_group}/{topk_group}/{top_k}", cfg, 8)
+
+
+def test_all_keys_equal_tie_rule():
+    """Router weight 0 and bias 0: every key is 0.5, so every token takes
+    experts 0..7 (groups 0..3, lower index first) with weight 1/8."""
+    dev = _dev()
+    cfg = _case(50, 256, 128)
+    x, rw, b, w = _inputs(cfg, 9, dev)
+    rw.zero_()
+    b.zero_()
+    out, r = run_forward(x, rw, b, w, cfg)
+    idx = r["topk_idx"].cpu().numpy()
+    assert np.array_equal(idx, np.tile(np.arange(8), (50, 1)))
+    assert torch.all(r["topk_w"] == 0.125)
+    cnt = r["expert_counts"].cpu().numpy()
+    assert cnt[:8].tolist() == [50] * 8 and cnt[8:].sum() == 0
+
+
+def test_route_entry_point_matches_forward():
+    dev = _dev()
+    cfg = _case(333, 512, 128)
+    x, rw, b, w = _inputs(cfg, 10, dev)
+    out, r = run_forward(x, rw, b, w, cfg)
+    rr = gl.route(x, rw, b, return_logits=True, return_counts=True)
+    torch.cuda.synchronize()
+    assert torch.equal(rr["topk_idx"], r["topk_idx"])
+    assert torch.equal(rr["topk_w"], r["topk_w"])
+    assert torch.equal(rr["router_logits"], r["router_logits"])
+    assert torch.equal(rr["expert_counts"], r["expert_counts"])
+
+
+def test_deterministic_and_token_permutation():
+    dev = _dev()
+    cfg = _case(600, 256, 128)
+    x, rw, b, w = _inputs(cfg, 11, dev)
+    o1, r1 = run_forward(x, rw, b, w, cfg)
+    o2, r2 = run_forward(x, rw, b, w, cfg)
+    assert torch.equal(o1, o2) and torch.equal(r1["topk_idx"], r2["topk_idx"])
+    perm = torch.randperm(600, generator=torch.Generator().manual_seed(0)).to(dev)
+    o3, r3 = run_forward(x[perm].contiguous(), rw, b, w, cfg)
+    assert torch.equal(r3["topk_idx"], r1["topk_idx"][perm])
+    assert torch.equal(o3, o1[perm])
+
+
+def test_single_token_and_empty():
+    dev = _dev()
+    cfg = _case(1, 256, 128)
+    _full_compare("T=1", cfg, 12)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    xs, rw, b, w = _inputs(cfg, 12, dev)
+    out = gl.forward(x, rw, b, w["w_gate"], w["w_up"], w["w_down"])
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256)
+
+
+# ---------------------------------------------------------------- full Beam shape
+@pytest.fixture(scope="module")
+def beam_bf16_weights():
+    dev = _dev()
+    cfg = workloads.workload("decode")
+    w = workloads.make_expert_weights(cfg, 0, dev)
+    torch.cuda.synchronize()
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+def _sample_tokens(r, near, T, hot=None, n=4):
+    idx = r["topk_idx"].cpu().numpy()
+    toks = list(range(min(n, T))) + [T - 1]
+    if hot is not None:
+        toks += list(np.nonzero(np.any(idx == hot, axis=1))[0][:2])
+    toks += list(np.nonzero(near)[0][:3])
+    return np.array(sorted(set(int(t) for t in toks)))
+
+
+def _full_shape(name, wl, w, extra=None):
+    dev = _dev()
+    cfg = workloads.workload(wl)
+    x, rw, b = workloads.make_small_inputs(cfg, 0)
+    x, rw, b = x.to(dev), rw.to(dev), b.to(dev)
+    out, r = run_forward(x, rw, b, w, cfg)
+    x64 = x.cpu().double().numpy()
+    rw64 = rw.cpu().double().numpy()
+    ora = oracle.route(x64, rw64, b.cpu().double().numpy(), 8, 4, 8)
+    rep = {"T": cfg["T"]}
+    near = check_routing(r, ora, cfg, rep)
+    cnt = r["expert_counts"].cpu().numpy()
+    rep["active_experts"] = int((cnt > 0).sum())
+    rep["max_over_mean"] = float(cnt.max() / cnt.mean())
+    tokens = _sample_tokens(r, near, cfg["T"], hot=int(cnt.argmax()))
+    ref = oracle_reference(tokens, x, rw, b, w, cfg, r["topk_idx"].cpu().numpy(), near)
+    check_outputs(out[torch.as_tensor(tokens, device=dev)].cpu().double().numpy(), ref, rep)
+    rep["sampled_tokens"] = len(tokens)
+    if extra:
+        extra(rep, cnt, out)
+    _report(name, rep)
+
+
+def test_beam_decode_full_shape(beam_bf16_weights):
+    _full_shape("decode T=64", "decode", beam_bf16_weights)
+
+
+def test_beam_prefill_full_shape(beam_bf16_weights):
+    def balanced(rep, cnt, out):
+        assert rep["max_over_mean"] <= 1.05
+    _full_shape("prefill T=4096", "prefill", beam_bf16_weights, balanced)
+
+
+def test_beam_skewed_full_shape(beam_bf16_weights):
+    def skewed(rep, cnt, out):
+        assert cnt[:8].min() >= 4 * cnt.mean()   # the +0.5 bias makes experts 0-7 hot
+        assert int(cnt.sum()) == 8 * 16384
+    _full_shape("skewed T=16384", "skewed", beam_bf16_weights, skewed)
+
+
+def test_beam_fp8_full_shape():
+    dev = _dev()
+    cfg = workloads.workload("fp8")
+    w8 = workloads.make_expert_weights(cfg, 0, dev)
+    torch.cuda.synchronize()
+    try:
+        _full_shape("fp8 T=8192", "fp8", w8)
+    finally:
+        del w8
+        torch.cuda.empty_cache()

@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of the Beam sparse-MoE block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+One step is one beam_moe_forward call over one batch of synthetic tokens,
+with the expert weights in the packed (MFMA fragment) layout made once at
+load time by beam_moe_pack_weights:
+router logits, group-limited selection, permutation, both grouped expert
+GEMMs and the combine. Inputs and the 20 GB of expert weights are resident
+in HBM before the timed region. The default workload is Beam's decode shape
+(T = 64 tokens, hidden 5120, 256 experts x SwiGLU 2560, bf16 weights); a
+second measurement at the prefill shape (T = 4096) is reported in the same
+line under "prefill".
+
+Printed fields beyond the usual ones:
+* roofline: the dominant kernel (the gate/up grouped GEMM), timed with HIP
+  events recorded by the library around its launches during the timed
+  region. achieved = algorithmic bytes (or flops) per launch / average
+  launch time; bytes = weights of the active experts + the x rows read + the
+  h rows written; flops = 4 * (T * top_k) * hidden * intermediate. The
+  bound is whichever of HBM (8 TB/s) and dense MFMA (bf16 2.5 PFLOP/s, fp8
+  5.0 PFLOP/s) takes longer for those figures. traffic: HBM bytes per
+  launch from the committed rocprofv3 counter summary for this kernel and
+  workload, scaled by the copy-kernel calibration stored with it; null when
+  the summary is missing or was taken from other kernel sources.
+* cpu_baseline: the oracle (numpy float64) on a bounded sample of the same
+  workload, on this machine's host cores.
+
+Other modes: --workload tiny|decode|prefill|skewed|fp8 picks the timed
+workload; --calibrate-copy runs one plain device copy of 1 GiB before the
+timed region (for counter calibration); --summarize DIR prints a summary of
+a rocprofv3 output directory (kernel stats or counter collection).
+"""
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at Beam shape (T=64 decode, T=4096 prefill) + % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+KERNEL_SOURCES = ["group_limited_routing_amd/csrc/expert_gemm.hip",
+                  "group_limited_routing_amd/csrc/common.h"]
+DOMINANT_KERNEL = "gemm_stream_kernel / gemm_tiled_kernel (gate/up pass)"
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def describe(cfg):
+    wdesc = "fp8 e4m3 weights, per-row scales" if cfg["w_dtype"] == "fp8" else "bf16 weights"
+    return (f"{cfg['name']}: T={cfg['T']} tokens, hidden {cfg['hidden']}, {cfg['n_experts']} experts "
+            f"x SwiGLU {cfg['intermediate']}, {wdesc}, x {cfg['x_dtype']}, group-limited top-{cfg['top_k']} "
+            f"({cfg['n_group']} groups, keep {cfg['topk_group']}), scale {cfg['routed_scaling_factor']}")
+
+
+def gateup_work(cfg, active):
+    """Algorithmic bytes and flops of one gate/up launch."""
+    T, H, I, k = cfg["T"], cfg["hidden"], cfg["intermediate"], cfg["top_k"]
+    wb = 1 if cfg["w_dtype"] == "fp8" else 2
+    xb = 4 if cfg["x_dtype"] == "f32" else 2
+    if cfg["w_dtype"] == "fp8":
+        x_read, h_write = T * H * 1, T * k * I * 4   # e4m3 x codes in, fp32 h out
+    else:
+        x_read, h_write = T * H * xb, T * k * I * 2
+    bytes_ = active * 2 * I * H * wb + x_read + h_write
+    flops = 4.0 * T * k * H * I
+    return bytes_, flops
+
+
+def layer_work(cfg, active):
+    """Algorithmic bytes and flops of the whole block (weights of active
+    experts + x + out + router weight; expert and router flops)."""
+    T, H, I, k, E = cfg["T"], cfg["hidden"], cfg["intermediate"], cfg["top_k"], cfg["n_experts"]
+    wb = 1 if cfg["w_dtype"] == "fp8" else 2
+    xb = 4 if cfg["x_dtype"] == "f32" else 2
+    bytes_ = active * 3 * I * H * wb + 2 * T * H * xb + E * H * 4
+    flops = 6.0 * T * k * H * I
+    return bytes_, flops
+
+
+def roofline(bytes_, flops, seconds, wdt, traffic=None):
+    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[wdt] * 1e12)
+    if t_hbm >= t_mfma:
+        ach = bytes_ / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+    ach = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS[wdt],
+            "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS[wdt], 4), "traffic": traffic}
+
+
+def stored_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary, or None
+    (missing, or counters taken on other kernel sources)."""
+    path = os.path.join(ROOT, "profiles", f"gateup_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class Bench:
+    def __init__(self, cfg, dev, weights=None, packed=None):
+        import torch
+        import group_limited_routing_amd as gl
+        import workloads
+        self.torch, self.gl = torch, gl
+        self.cfg = cfg
+        x, rw, b = workloads.make_small_inputs(cfg, 0)
+        self.x, self.rw, self.b = x.to(dev), rw.to(dev), b.to(dev)
+        self.w = weights if weights is not None else workloads.make_expert_weights(cfg, 0, dev)
+        # the MFMA fragment copy the timed forward reads (packed once, at load)
+        self.pw = packed if packed is not None else {
+            k: gl.pack_weights(self.w[k]) for k in ("w_gate", "w_up", "w_down")}
+        w = self.w
+        self.scales = None
+        if w["w_gate"].dtype == torch.float8_e4m3fn:
+            self.scales = (w["w_gate_scale"], w["w_up_scale"], w["w_down_scale"])
+        xdt = self.x.dtype
+        wdt = w["w_gate"].dtype
+        c = gl.make_config(cfg["hidden"], cfg["intermediate"], cfg["n_experts"], cfg["n_group"],
+                           cfg["topk_group"], cfg["top_k"], cfg["routed_scaling_factor"], xdt, wdt,
+                           packed=True)
+        self.ws = torch.empty(gl.workspace_bytes(c, cfg["T"]), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(self.x)
+        r = gl.route(self.x, self.rw, self.b, n_group=cfg["n_group"], topk_group=cfg["topk_group"],
+                     top_k=cfg["top_k"], return_counts=True, workspace=self.ws)
+        cnt = r["expert_counts"].cpu()
+        self.active = int((cnt > 0).sum())
+        self.max_over_mean = float(cnt.max().item() / cnt.float().mean().item())
+
+    def step(self):
+        w = self.pw
+        self.gl.forward(self.x, self.rw, self.b, w["w_gate"], w["w_up"], w["w_down"],
+                        scales=self.scales, packed=True, n_group=self.cfg["n_group"],
+                        topk_group=self.cfg["topk_group"], top_k=self.cfg["top_k"],
+                        routed_scaling_factor=self.cfg["routed_scaling_factor"], out=self.out,
+                        workspace=self.ws)
+
+    def run(self, steps, warmup):
+        torch, gl = self.torch, self.gl
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        gl.profile_begin(["gateup"])
+        t0 = time.perf_counter()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            self.step()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        prof = gl.profile_end()
+        ms_step = e0.elapsed_time(e1) / steps
+        gu_ms, gu_n = prof["gateup"]
+        # per-stage breakdown from a short separate pass (events on every stage)
+        gl.profile_begin()
+        for _ in range(min(steps, 10)):
+            self.step()
+        torch.cuda.synchronize()
+        stages = {k: round(v[0] / v[1], 4) for k, v in gl.profile_end().items()}
+        return {"ms_per_step": ms_step, "wall_s": wall, "gateup_ms": gu_ms / gu_n, "stages_ms": stages}
+
+
+def cpu_baseline(cfg, bench, n_tokens):
+    """The oracle on the first n_tokens tokens of the same inputs (float64)."""
+    import numpy as np
+    import torch
+    import oracle
+    tok = np.arange(n_tokens)
+    x64 = bench.x[:n_tokens].cpu().double().numpy()
+    rw64 = bench.rw.cpu().double().numpy()
+    b64 = bench.b.cpu().double().numpy()
+    r = oracle.route(x64, rw64, b64, cfg["n_group"], cfg["topk_group"], cfg["top_k"])
+    need = sorted(set(int(e) for e in np.unique(r["idx"])))
+    fp8 = cfg["w_dtype"] == "fp8"
+    host = {}
+    for e in need:  # copy the needed experts to host memory before timing
+        host[e] = {k: bench.w[k][e].cpu() for k in ("w_gate", "w_up", "w_down")}
+        if fp8:
+            for k in ("w_gate", "w_up", "w_down"):
+                host[e][k + "_scale"] = bench.w[k + "_scale"][e].cpu()
+
+    def get(e):
+        if fp8:
+            return tuple(oracle.e4m3.decode(host[e][k].view(torch.uint8).numpy())
+                         * host[e][k + "_scale"].double().numpy()[:, None]
+                         for k in ("w_gate", "w_up", "w_down"))
+        return tuple(host[e][k].double().numpy() for k in ("w_gate", "w_up", "w_down"))
+
+    t0 = time.perf_counter()
+    oracle.forward_tokens(tok, bench.x.cpu().double().numpy(), rw64, b64, get,
+                          n_group=cfg["n_group"], topk_group=cfg["topk_group"], top_k=cfg["top_k"],
+                          routed_scaling_factor=cfg["routed_scaling_factor"], fp8=fp8)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of the {cfg['name']} workload ({len(need)} experts), "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
+def summarize(d):
+    """Print kernel statistics / counters found under a rocprofv3 output dir."""
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        print(f"# kernel stats: {os.path.relpath(path, d)}")
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")
+        for r in rows:
+            print(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.1f} {float(r['MinNs']) / 1e3:>10.1f} "
+                  f"{float(r['MaxNs']) / 1e3:>10.1f} {float(r['Percentage']):>6.2f}  {r['Name'][:110]}")
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        print(f"# counters: {os.path.relpath(path, d)}")
+        agg = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"][:110], r["Counter_Name"])
+                a = agg.setdefault(key, [0.0, 0])
+                a[0] += float(r["Counter_Value"])
+                a[1] += 1
+        print(f"{'dispatches':>10} {'mean_per_dispatch':>20}  counter  kernel")
+        for (kname, cname), (tot, n) in sorted(agg.items()):
+            print(f"{n:>10} {tot / n:>20.1f}  {cname}  {kname}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skewed", "fp8"])
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU: the MoE block here runs on a single MI355X "
+              "(expert-parallel sharding across GPUs is not part of this build); "
+              "run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    cfg = workloads.workload(args.workload)
+    bench = Bench(cfg, dev)
+    res = bench.run(args.steps, args.warmup)
+    wdt = "fp8" if cfg["w_dtype"] == "fp8" else "bf16"
+    gb, gf = gateup_work(cfg, bench.active)
+    rl = roofline(gb, gf, res["gateup_ms"] / 1e3, wdt, stored_traffic(cfg["name"]))
+    lb, lf = layer_work(cfg, bench.active)
+    step_s = res["ms_per_step"] / 1e3
+    line = {
+        "metric": METRIC,
+        "value": round(cfg["T"] / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wdt,
+        "data": "synthetic",
+        "config": {"workload": describe(cfg), "T": cfg["T"], "hidden": cfg["hidden"],
+                   "intermediate": cfg["intermediate"], "n_experts": cfg["n_experts"],
+                   "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "top_k": cfg["top_k"],
+                   "active_experts": bench.active, "max_over_mean_load": round(bench.max_over_mean, 4),
+                   "parallelism": "single GPU"},
+        "roofline": dict(rl, kernel=DOMINANT_KERNEL, launch_ms=round(res["gateup_ms"], 4),
+                         algorithmic_bytes=gb, algorithmic_flops=gf),
+        "layer": {"pct_hbm": round(lb / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "pct_mfma": round(lf / step_s / 1e12 / MFMA_PEAK_TFLOPS[wdt], 4),
+                  "algorithmic_bytes": lb, "flops": lf, "stages_ms": res["stages_ms"]},
+    }
+    if args.workload == "decode" and not args.no_prefill:
+        pcfg = workloads.workload("prefill")
+        pb = Bench(pcfg, dev, weights=bench.w, packed=bench.pw)
+        pres = pb.run(args.prefill_steps, 3)
+        pgb, pgf = gateup_work(pcfg, pb.active)
+        plb, plf = layer_work(pcfg, pb.active)
+        ps = pres["ms_per_step"] / 1e3
+        line["prefill"] = {
+            "workload": describe(pcfg), "value": round(pcfg["T"] / ps, 1), "unit": "tokens/s",
+            "ms_per_step": round(pres["ms_per_step"], 4), "steps": args.prefill_steps,
+            "max_over_mean_load": round(pb.max_over_mean, 4),
+            "roofline": dict(roofline(pgb, pgf, pres["gateup_ms"] / 1e3, "bf16", stored_traffic("prefill")),
+                             launch_ms=round(pres["gateup_ms"], 4)),
+            "layer": {"pct_hbm": round(plb / ps / 1e9 / HBM_PEAK_GBS, 4),
+                      "pct_mfma": round(plf / ps / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                      "stages_ms": pres["stages_ms"]},
+        }
+        del pb
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, bench, min(args.cpu_tokens, cfg["T"]))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -21,9 +21,14 @@ LIB_PATH = os.path.join(HERE, "libbeam_moe.so")
 BEAM_OK, BEAM_ERR_NULL, BEAM_ERR_CONFIG, BEAM_ERR_SHAPE = 0, 1, 2, 3
 BEAM_ERR_DTYPE, BEAM_ERR_ALIGN, BEAM_ERR_WORKSPACE, BEAM_ERR_HIP = 4, 5, 6, 7
 BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
+BEAM_LAYOUT_ROW_MAJOR, BEAM_LAYOUT_PACKED = 0, 1
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_forward",
-            "beam_moe_status_string")
+            "beam_moe_status_string", "beam_moe_profile_begin", "beam_moe_profile_end",
+            "beam_moe_pack_weights")
+
+STAGES = ("router_logits", "select", "perm_hist", "perm_scan", "perm_scatter", "quant_x",
+          "gateup", "quant_h", "down", "combine")
 
 
 class BeamMoeConfig(ctypes.Structure):
@@ -37,6 +42,7 @@ class BeamMoeConfig(ctypes.Structure):
         ("routed_scaling_factor", ctypes.c_float),
         ("x_dtype", ctypes.c_int32),
         ("w_dtype", ctypes.c_int32),
+        ("w_layout", ctypes.c_int32),
     ]
 
 
@@ -68,6 +74,12 @@ def lib():
         L.beam_moe_forward.restype = ctypes.c_int
         L.beam_moe_status_string.argtypes = [i32]
         L.beam_moe_status_string.restype = ctypes.c_char_p
+        L.beam_moe_profile_begin.argtypes = [ctypes.c_uint32]
+        L.beam_moe_profile_begin.restype = ctypes.c_int
+        L.beam_moe_profile_end.argtypes = [vp, vp]
+        L.beam_moe_profile_end.restype = ctypes.c_int
+        L.beam_moe_pack_weights.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+        L.beam_moe_pack_weights.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -81,11 +93,28 @@ _W_DTYPES = {torch.bfloat16: BEAM_BF16, torch.float8_e4m3fn: BEAM_FP8_E4M3}
 
 
 def make_config(hidden, intermediate, n_experts=256, n_group=8, topk_group=4, top_k=8,
-                routed_scaling_factor=2.5, x_dtype=torch.bfloat16, w_dtype=torch.bfloat16):
+                routed_scaling_factor=2.5, x_dtype=torch.bfloat16, w_dtype=torch.bfloat16,
+                packed=False):
     if x_dtype not in _X_DTYPES or w_dtype not in _W_DTYPES:
         raise TypeError(f"unsupported dtypes x={x_dtype} w={w_dtype}")
     return BeamMoeConfig(hidden, intermediate, n_experts, n_group, topk_group, top_k,
-                         routed_scaling_factor, _X_DTYPES[x_dtype], _W_DTYPES[w_dtype])
+                         routed_scaling_factor, _X_DTYPES[x_dtype], _W_DTYPES[w_dtype],
+                         BEAM_LAYOUT_PACKED if packed else BEAM_LAYOUT_ROW_MAJOR)
+
+
+def pack_weights(w, out=None, stream=None):
+    """MFMA-fragment copy of row-major expert weights w [E, R, C] (bf16 or
+    float8_e4m3fn); pass the result to forward(..., packed=True)."""
+    if w.dim() != 3 or not w.is_contiguous() or w.dtype not in _W_DTYPES:
+        raise ValueError("pack_weights needs a contiguous [E, rows, cols] bf16/fp8 tensor")
+    if out is None:
+        out = torch.empty_like(w)
+    E, R, C = w.shape
+    st = lib().beam_moe_pack_weights(_ptr(w), _ptr(out), E, R, C, _W_DTYPES[w.dtype],
+                                     _stream(w.device, stream))
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_pack_weights")
+    return out
 
 
 def workspace_bytes(cfg, T):
@@ -145,10 +174,11 @@ def route(x, router_w, expert_bias, *, n_group=8, topk_group=4, top_k=8,
 
 def forward(x, router_w, expert_bias, w_gate, w_up, w_down, *, scales=None, n_group=8,
             topk_group=4, top_k=8, routed_scaling_factor=2.5, out=None, return_routing=False,
-            return_logits=False, workspace=None, stream=None):
+            return_logits=False, workspace=None, stream=None, packed=False):
     """The whole MoE block. ``scales`` = (w_gate_scale, w_up_scale, w_down_scale)
-    for fp8 weights. Returns out [T, H] (x's dtype), or (out, routing dict) with
-    ``return_routing``."""
+    for fp8 weights; ``packed`` says the weights come from pack_weights().
+    Returns out [T, H] (x's dtype), or (out, routing dict) with
+    ``return_routing`` or ``return_logits``."""
     T, H = x.shape
     E = router_w.shape[0]
     I = w_gate.shape[1]
@@ -169,7 +199,7 @@ def forward(x, router_w, expert_bias, w_gate, w_up, w_down, *, scales=None, n_gr
         _check(su, "w_up_scale", (E, I), (torch.float32,), dev)
         _check(sd, "w_down_scale", (E, H), (torch.float32,), dev)
     cfg = make_config(H, I, E, n_group, topk_group, top_k, routed_scaling_factor, x.dtype,
-                      w_gate.dtype)
+                      w_gate.dtype, packed)
     if out is None:
         out = torch.empty((T, H), dtype=x.dtype, device=dev)
     else:
@@ -192,3 +222,24 @@ def forward(x, router_w, expert_bias, w_gate, w_up, w_down, *, scales=None, n_gr
         return out, {"topk_idx": idx, "topk_w": w, "expert_counts": counts,
                      "router_logits": logits}
     return out
+
+
+def profile_begin(stages=STAGES):
+    """Start timing the named stages of every following route/forward call."""
+    mask = 0
+    for name in stages:
+        mask |= 1 << STAGES.index(name)
+    st = lib().beam_moe_profile_begin(mask)
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_profile_begin")
+
+
+def profile_end():
+    """Stop timing; returns {stage: (total_ms, launches)} for timed stages."""
+    n = len(STAGES)
+    tot = (ctypes.c_float * n)()
+    cnt = (ctypes.c_int32 * n)()
+    st = lib().beam_moe_profile_end(ctypes.cast(tot, ctypes.c_void_p), ctypes.cast(cnt, ctypes.c_void_p))
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_profile_end")
+    return {STAGES[i]: (float(tot[i]), int(cnt[i])) for i in range(n) if cnt[i] > 0}

@@ -5,6 +5,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include "common.h"
 #include "internal.h"
 
@@ -72,6 +75,8 @@ beam_status check_config(const beam_moe_config* c) {
   if (!isfinite(c->routed_scaling_factor)) return BEAM_ERR_CONFIG;
   if (c->x_dtype != BEAM_F32 && c->x_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
   if (c->w_dtype != BEAM_BF16 && c->w_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
+  if (c->w_layout != BEAM_LAYOUT_ROW_MAJOR && c->w_layout != BEAM_LAYOUT_PACKED)
+    return BEAM_ERR_CONFIG;
   if (c->hidden <= 0 || c->hidden % 128 != 0 || c->hidden > 65536) return BEAM_ERR_SHAPE;
   if (c->intermediate <= 0 || c->intermediate % 128 != 0 || c->intermediate > 65536)
     return BEAM_ERR_SHAPE;
@@ -90,14 +95,68 @@ Shape shape_of(const beam_moe_config* c, int32_t T) {
   s.rsf = c->routed_scaling_factor;
   s.x_f32 = c->x_dtype == BEAM_F32;
   s.w_fp8 = c->w_dtype == BEAM_FP8_E4M3;
+  s.w_packed = c->w_layout == BEAM_LAYOUT_PACKED;
   return s;
 }
 
 bool misaligned(const void* p) { return p && (((uintptr_t)p) & 15u) != 0; }
 
-#define BEAM_LAUNCH(call)                      \
-  do {                                         \
-    if ((call) != hipSuccess) return BEAM_ERR_HIP; \
+// Optional stage timing (beam_moe_profile_begin / _end): a pair of HIP
+// events around each selected stage's launch, on the call's stream.
+struct Profiler {
+  struct Rec {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::mutex mu;
+  bool on = false;
+  uint32_t mask = 0;
+  std::vector<Rec> recs;
+
+  void release() {
+    for (auto& r : recs) {
+      hipEventDestroy(r.a);
+      hipEventDestroy(r.b);
+    }
+    recs.clear();
+  }
+};
+Profiler g_prof;
+
+template <typename F>
+beam_status staged(int stage, hipStream_t st, F&& launch) {
+  bool timed;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    timed = g_prof.on && ((g_prof.mask >> stage) & 1u);
+  }
+  hipEvent_t a = nullptr, b = nullptr;
+  if (timed) {
+    if (hipEventCreate(&a) != hipSuccess) return BEAM_ERR_HIP;
+    if (hipEventCreate(&b) != hipSuccess || hipEventRecord(a, st) != hipSuccess) {
+      hipEventDestroy(a);
+      if (b) hipEventDestroy(b);
+      return BEAM_ERR_HIP;
+    }
+  }
+  const hipError_t le = launch();
+  if (timed) {
+    const hipError_t re = hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (le == hipSuccess && re == hipSuccess) {
+      g_prof.recs.push_back({stage, a, b});
+    } else {
+      hipEventDestroy(a);
+      hipEventDestroy(b);
+    }
+  }
+  return le == hipSuccess ? BEAM_OK : BEAM_ERR_HIP;
+}
+
+#define STAGE(id, call)                                                        \
+  do {                                                                         \
+    const beam_status stage_status_ = staged((id), st, [&]() { return (call); }); \
+    if (stage_status_ != BEAM_OK) return stage_status_;                        \
   } while (0)
 
 // Routing and permutation shared by route and forward. Fills the sorted
@@ -173,11 +232,11 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
   hipStream_t st = (hipStream_t)stream;
   Buffers B = carve(L, workspace);
   float* z = router_logits ? router_logits : B.z;
-  BEAM_LAUNCH(launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
-  BEAM_LAUNCH(launch_select(z, expert_bias, T, s.n_group, s.topk_group, s.top_k, topk_idx, topk_w, st));
+  STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
+  STAGE(BEAM_STAGE_SELECT, launch_select(z, expert_bias, T, s.n_group, s.topk_group, s.top_k, topk_idx, topk_w, st));
   if (expert_counts) {
-    BEAM_LAUNCH(launch_perm_hist(topk_idx, T, s.top_k, B.chist, st));
-    BEAM_LAUNCH(launch_perm_scan(B.chist, L.nchunks, kTiledBM, B.cbase, B.counts, B.offsets,
+    STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(topk_idx, T, s.top_k, B.chist, st));
+    STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, kTiledBM, B.cbase, B.counts, B.offsets,
                                  B.meta, B.tile_e, B.tile_r, expert_counts, st));
   }
   return BEAM_OK;
@@ -217,12 +276,12 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
   const int k = s.top_k;
   const int BM = use_stream_gemm(s) ? kStreamBM : kTiledBM;
 
-  BEAM_LAUNCH(launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
-  BEAM_LAUNCH(launch_select(z, expert_bias, T, s.n_group, s.topk_group, k, idx, w, st));
-  BEAM_LAUNCH(launch_perm_hist(idx, T, k, B.chist, st));
-  BEAM_LAUNCH(launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts, B.offsets, B.meta,
+  STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
+  STAGE(BEAM_STAGE_SELECT, launch_select(z, expert_bias, T, s.n_group, s.topk_group, k, idx, w, st));
+  STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(idx, T, k, B.chist, st));
+  STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts, B.offsets, B.meta,
                                B.tile_e, B.tile_r, expert_counts_out, st));
-  BEAM_LAUNCH(launch_perm_scatter(idx, w, T, k, s.rsf, B.cbase, B.offsets, B.stok, B.sw, B.inv, st));
+  STAGE(BEAM_STAGE_PERM_SCATTER, launch_perm_scatter(idx, w, T, k, s.rsf, B.cbase, B.offsets, B.stok, B.sw, B.inv, st));
 
   GemmArgs g{};
   g.tile_e = B.tile_e;
@@ -241,7 +300,7 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
     float* hf = (float*)(ws + L.h);
     float* hs = (float*)(ws + L.hs);
     uint8_t* hq = ws + L.hq;
-    BEAM_LAUNCH(launch_quant_x(x, s.x_f32, T, s.H, k, xq, xs, hamax, st));
+    STAGE(BEAM_STAGE_QUANT_X, launch_quant_x(x, s.x_f32, T, s.H, k, xq, xs, hamax, st));
     g.a = xq;
     g.a_scale = xs;
     g.w0 = w_gate;
@@ -252,8 +311,8 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
     g.hamax = hamax;
     g.K = s.H;
     g.N = s.I;
-    BEAM_LAUNCH(launch_gateup(s, g, st));
-    BEAM_LAUNCH(launch_quant_h(hf, hamax, T * k, s.I, hq, hs, st));
+    STAGE(BEAM_STAGE_GATEUP, launch_gateup(s, g, st));
+    STAGE(BEAM_STAGE_QUANT_H, launch_quant_h(hf, hamax, T * k, s.I, hq, hs, st));
     g.a = hq;
     g.a_scale = hs;
     g.w0 = w_down;
@@ -264,7 +323,7 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
     g.hamax = nullptr;
     g.K = s.I;
     g.N = s.H;
-    BEAM_LAUNCH(launch_down(s, g, st));
+    STAGE(BEAM_STAGE_DOWN, launch_down(s, g, st));
   } else {
     void* h = ws + L.h;
     g.a = x;
@@ -273,17 +332,63 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
     g.out = h;
     g.K = s.H;
     g.N = s.I;
-    BEAM_LAUNCH(launch_gateup(s, g, st));
+    STAGE(BEAM_STAGE_GATEUP, launch_gateup(s, g, st));
     g.a = h;
     g.w0 = w_down;
     g.w1 = nullptr;
     g.out = y;
     g.K = s.I;
     g.N = s.H;
-    BEAM_LAUNCH(launch_down(s, g, st));
+    STAGE(BEAM_STAGE_DOWN, launch_down(s, g, st));
   }
-  BEAM_LAUNCH(launch_combine(y, B.inv, T, k, s.H, s.x_f32, out, st));
+  STAGE(BEAM_STAGE_COMBINE, launch_combine(y, B.inv, T, k, s.H, s.x_f32, out, st));
   return BEAM_OK;
+}
+
+beam_status beam_moe_pack_weights(const void* src, void* dst, int32_t n_experts, int32_t rows,
+                                  int32_t cols, int32_t w_dtype, void* stream) {
+  if (!src || !dst) return BEAM_ERR_NULL;
+  if (w_dtype != BEAM_BF16 && w_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
+  if (n_experts < 1 || rows < 16 || rows % 16 != 0 || cols < 128 || cols % 128 != 0)
+    return BEAM_ERR_SHAPE;
+  const long long bytes = (long long)n_experts * rows * cols * (w_dtype == BEAM_BF16 ? 2 : 1);
+  if (bytes > (1LL << 40)) return BEAM_ERR_SHAPE;
+  if (misaligned(src) || misaligned(dst)) return BEAM_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  return launch_pack(src, dst, n_experts, rows, cols, w_dtype == BEAM_FP8_E4M3, st) == hipSuccess
+             ? BEAM_OK
+             : BEAM_ERR_HIP;
+}
+
+beam_status beam_moe_profile_begin(uint32_t stage_mask) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.release();
+  g_prof.mask = stage_mask;
+  g_prof.on = true;
+  return BEAM_OK;
+}
+
+beam_status beam_moe_profile_end(float* total_ms, int32_t* launches) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  float tot[BEAM_STAGE_COUNT] = {};
+  int32_t cnt[BEAM_STAGE_COUNT] = {};
+  beam_status st = BEAM_OK;
+  for (auto& r : g_prof.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = BEAM_ERR_HIP;
+      continue;
+    }
+    tot[r.stage] += ms;
+    cnt[r.stage] += 1;
+  }
+  g_prof.release();
+  g_prof.on = false;
+  for (int i = 0; i < BEAM_STAGE_COUNT; ++i) {
+    if (total_ms) total_ms[i] = tot[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return st;
 }
 
 }  // extern "C"

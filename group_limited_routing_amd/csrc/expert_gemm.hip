@@ -83,6 +83,7 @@ __device__ __forceinline__ OpReg<FP8> load_op(const void* p) {
   }
 }
 
+
 // The A operand of a bf16 pass may be stored as fp32 (x in fp32); it is then
 // rounded to bf16 (nearest even) on load. 8 values per lane.
 template <typename AT>
@@ -182,7 +183,7 @@ __device__ __forceinline__ void row_amax_update(uint32_t* hamax, int grow, float
 // ---------------------------------------------------------------- stream variant
 // FN = 16-row weight fragments per wave (mode 0: FN/2 gate + FN/2 up),
 // D = depth of the register prefetch ring (in MFMA k-steps).
-template <int MODE, typename AT, bool FP8, int FN, int D>
+template <int MODE, typename AT, bool FP8, bool PACKED, int FN, int D>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
   using WT = typename WTraits<FP8>::W;
   constexpr int KSTEP = WTraits<FP8>::KSTEP;
@@ -215,8 +216,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
       n = ncol0 + f * 16 + r;
       W = (const WT*)p.w0;
     }
-    brow[f] = W + ((size_t)ti.e * N + n) * K + LANE_K * g;
+    if (PACKED)  // fragment block (n / 16, step) starts at ((n/16) * K/KSTEP + step) * 16*KSTEP
+      brow[f] = W + (size_t)ti.e * N * K + (size_t)((n - r) >> 4) * 16 * K + lane * LANE_K;
+    else
+      brow[f] = W + ((size_t)ti.e * N + n) * K + LANE_K * g;
   }
+  constexpr int BSTEP = PACKED ? 16 * KSTEP : KSTEP;  // elements between k-steps of a lane
 
   f32x4 acc[FN];
 #pragma unroll
@@ -234,27 +239,43 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
     else
       aq16[d].load((const typename std::conditional<FP8, uint16_t, AT>::type*)arow + (size_t)s * KSTEP);
 #pragma unroll
-    for (int f = 0; f < FN; ++f) bq[d][f] = load_op<FP8>(brow[f] + (size_t)s * KSTEP);
+    for (int f = 0; f < FN; ++f) bq[d][f] = load_op<FP8>(brow[f] + (size_t)s * BSTEP);
   };
+  auto consume = [&](int d) {
+    OR a;
+    if constexpr (FP8)
+      a = aq8[d];
+    else
+      a = aq16[d].bits();
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < nks) load_step(d, d);
-  for (int s0 = 0; s0 < nks; s0 += D) {
+    for (int f = 0; f < FN; ++f) acc[f] = mfma_op(a, bq[d][f], acc[f]);
+  };
+  // Prologue without branches (a step past the end, possible only when
+  // K < D * KSTEP, re-reads the last step and is never consumed).
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_step(d, min(d, nks - 1));
+  // Steady state without branches around the loads, so the compiler's wait
+  // counts let each step wait only for its own (oldest) loads while the
+  // next D-1 steps stay in flight.
+  int s0 = 0;
+  for (; s0 + 2 * D <= nks; s0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (s0 + d < nks) {
-        OR a;
-        if constexpr (FP8)
-          a = aq8[d];
-        else
-          a = aq16[d].bits();
-#pragma unroll
-        for (int f = 0; f < FN; ++f) acc[f] = mfma_op(a, bq[d][f], acc[f]);
-        const int sn = s0 + d + D;
-        if (sn < nks) load_step(d, sn);
-      }
+      consume(d);
+      load_step(d, s0 + d + D);
     }
   }
+  // Tail: at most 2D - 1 steps left, D of them already loaded.
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (s0 + d < nks) {
+      consume(d);
+      if (s0 + d + D < nks) load_step(d, s0 + d + D);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (s0 + D + d < nks) consume(d);
 
   if (MODE == 0) {
 #pragma unroll
@@ -296,7 +317,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
 // 16 rows of one MFMA operand read spread over all banks.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
-template <int MODE, typename AT, bool FP8>
+template <int MODE, typename AT, bool FP8, bool PACKED>
 __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
   using WT = typename WTraits<FP8>::W;
   constexpr int BM = kTiledBM, NBR = 128;
@@ -318,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
   // Global -> LDS assignment: 1024 chunks of A and of B per stage, 4 each per thread.
   const AT* agp[4];
   const WT* bgp[4];
-  int soff[4];
+  int soff[4], boff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = tid + 256 * i, lr = q >> 3, c = q & 7;
@@ -334,8 +355,20 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
       W = (const WT*)p.w0;
       n = n0 + lr;
     }
-    bgp[i] = W + ((size_t)ti.e * N + n) * K + c * CH;
     soff[i] = swz(lr, c);
+    if (PACKED) {
+      // The stage's B tile is 8 row blocks x (128 bytes of k) of fragment
+      // blocks; chunk q of it is 16 contiguous bytes, and it goes to LDS
+      // linearly at q * 16. Row block rb = q / 128 covers tile rows 16 rb..
+      const int rb = q >> 7, within = q & 127;
+      const int nb = (MODE == 0) ? n0 + 16 * (rb & 3) : n0 + 16 * rb;
+      const WT* Wb = (const WT*)((MODE == 0) ? (rb < 4 ? p.w0 : p.w1) : p.w0);
+      bgp[i] = Wb + (size_t)ti.e * N * K + (size_t)(nb >> 4) * 16 * K + within * CH;
+      boff[i] = q * 16;
+    } else {
+      bgp[i] = W + ((size_t)ti.e * N + n) * K + c * CH;
+      boff[i] = soff[i];
+    }
   }
 
   int arow_l[4], brow_l[4];
@@ -362,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
         ra[i].v = ld16(agp[i] + (size_t)kt * BK);
       else
         ra[i].load(agp[i] + (size_t)kt * BK);
-      rb[i] = ld16(bgp[i] + (size_t)kt * BK);
+      rb[i] = ld16(bgp[i] + (size_t)kt * (PACKED ? 16 * BK : BK));
     }
   };
   auto lstore = [&](int buf) {
@@ -370,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       st16(base + soff[i], ra[i].bits());
-      st16(base + A_BYTES + soff[i], rb[i]);
+      st16(base + A_BYTES + boff[i], rb[i]);
     }
   };
 
@@ -390,8 +423,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
       for (int f = 0; f < 4; ++f) {
         af[f].lo = ld16(As + swz(arow_l[f], 2 * g));
         af[f].hi = ld16(As + swz(arow_l[f], 2 * g + 1));
-        bfr[f].lo = ld16(Bs + swz(brow_l[f], 2 * g));
-        bfr[f].hi = ld16(Bs + swz(brow_l[f], 2 * g + 1));
+        if (PACKED) {  // fragment block of row block brow_l / 16: 64 lanes x 32 bytes
+          const uint8_t* blk = Bs + (brow_l[f] >> 4) * 2048 + lane * 32;
+          bfr[f].lo = ld16(blk);
+          bfr[f].hi = ld16(blk + 16);
+        } else {
+          bfr[f].lo = ld16(Bs + swz(brow_l[f], 2 * g));
+          bfr[f].hi = ld16(Bs + swz(brow_l[f], 2 * g + 1));
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -404,7 +443,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           af[f] = ld16(As + swz(arow_l[f], s * 4 + g));
-          bfr[f] = ld16(Bs + swz(brow_l[f], s * 4 + g));
+          // packed: row block brow_l / 16 holds two 1 KB k-step blocks per stage
+          bfr[f] = PACKED ? ld16(Bs + ((brow_l[f] >> 4) * 2 + s) * 1024 + lane * 16)
+                          : ld16(Bs + swz(brow_l[f], s * 4 + g));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -467,61 +508,94 @@ bool use_stream_gemm(const Shape& s) {
   return (long long)s.T * s.top_k <= 16LL * s.E;
 }
 
-template <int MODE, typename AT, bool FP8>
+// Output columns per workgroup: 4 waves x 16 x FN (down) or x 16 x FN/2
+// (gate/up). FN = 8 where it divides N, else 4, else 2 (N is a multiple of 128).
+template <int MODE, typename AT, bool FP8, bool PACKED>
 static void launch_stream(const Shape& s, const GemmArgs& g, hipStream_t st) {
-  constexpr int D = FP8 ? 2 : 4;
-  if (MODE == 0) {
-    dim3 grid(mtile_bound(s, kStreamBM) * (g.N / 128));
-    gemm_stream_kernel<0, AT, FP8, 4, D><<<grid, 256, 0, st>>>(g);
-  } else if (g.N % 256 == 0) {
-    dim3 grid(mtile_bound(s, kStreamBM) * (g.N / 256));
-    gemm_stream_kernel<1, AT, FP8, 4, D><<<grid, 256, 0, st>>>(g);
-  } else {
-    dim3 grid(mtile_bound(s, kStreamBM) * (g.N / 128));
-    gemm_stream_kernel<1, AT, FP8, 2, D><<<grid, 256, 0, st>>>(g);
-  }
+  constexpr int D = 2;
+  const int per = (MODE == 0) ? 32 : 64;  // columns per workgroup per unit of FN
+  const int fn = (g.N % (8 * per) == 0) ? 8 : (g.N % (4 * per) == 0) ? 4 : 2;
+  dim3 grid(mtile_bound(s, kStreamBM) * (g.N / (fn * per)));
+  if (fn == 8)
+    gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, D><<<grid, 256, 0, st>>>(g);
+  else if (fn == 4)
+    gemm_stream_kernel<MODE, AT, FP8, PACKED, 4, D><<<grid, 256, 0, st>>>(g);
+  else
+    gemm_stream_kernel<MODE, AT, FP8, PACKED, 2, D><<<grid, 256, 0, st>>>(g);
+}
+
+template <int MODE, typename AT, bool FP8, bool PACKED>
+static void launch_tiled(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  dim3 grid(mtile_bound(s, kTiledBM) * (g.N / (MODE == 0 ? 64 : 128)));
+  gemm_tiled_kernel<MODE, AT, FP8, PACKED><<<grid, 256, 0, st>>>(g);
 }
 
 template <int MODE, typename AT, bool FP8>
-static void launch_tiled(const Shape& s, const GemmArgs& g, hipStream_t st) {
-  dim3 grid(mtile_bound(s, kTiledBM) * (g.N / (MODE == 0 ? 64 : 128)));
-  gemm_tiled_kernel<MODE, AT, FP8><<<grid, 256, 0, st>>>(g);
+static void launch_variant(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  const bool stream = use_stream_gemm(s);
+  if (s.w_packed) {
+    if (stream)
+      launch_stream<MODE, AT, FP8, true>(s, g, st);
+    else
+      launch_tiled<MODE, AT, FP8, true>(s, g, st);
+  } else {
+    if (stream)
+      launch_stream<MODE, AT, FP8, false>(s, g, st);
+    else
+      launch_tiled<MODE, AT, FP8, false>(s, g, st);
+  }
 }
 
 hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st) {
-  const bool stream = use_stream_gemm(s);
-  if (s.w_fp8) {
-    if (stream)
-      launch_stream<0, uint8_t, true>(s, g, st);
-    else
-      launch_tiled<0, uint8_t, true>(s, g, st);
-  } else if (s.x_f32) {
-    if (stream)
-      launch_stream<0, float, false>(s, g, st);
-    else
-      launch_tiled<0, float, false>(s, g, st);
-  } else {
-    if (stream)
-      launch_stream<0, uint16_t, false>(s, g, st);
-    else
-      launch_tiled<0, uint16_t, false>(s, g, st);
-  }
+  if (s.w_fp8)
+    launch_variant<0, uint8_t, true>(s, g, st);
+  else if (s.x_f32)
+    launch_variant<0, float, false>(s, g, st);
+  else
+    launch_variant<0, uint16_t, false>(s, g, st);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const Shape& s, const GemmArgs& g, hipStream_t st) {
-  const bool stream = use_stream_gemm(s);
-  if (s.w_fp8) {
-    if (stream)
-      launch_stream<1, uint8_t, true>(s, g, st);
-    else
-      launch_tiled<1, uint8_t, true>(s, g, st);
-  } else {
-    if (stream)
-      launch_stream<1, uint16_t, false>(s, g, st);
-    else
-      launch_tiled<1, uint16_t, false>(s, g, st);
-  }
+  if (s.w_fp8)
+    launch_variant<1, uint8_t, true>(s, g, st);
+  else
+    launch_variant<1, uint16_t, false>(s, g, st);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- weight packing
+// Row-major [rows, cols] matrices (cols = the reduction) to the MFMA fragment
+// layout: one block per (16-row block, k-step) holding the 64 lanes' operand
+// bytes in lane order (lane l: row l % 16, k-step bytes (l / 16) * LB ..).
+// SB = bytes of one k-step of one row (64 for bf16, 128 for fp8), LB = SB / 4.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ src,
+                                                   uint8_t* __restrict__ dst, long long chunks,
+                                                   long long mat_bytes, int row_bytes, int SB) {
+  const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const long long o = c * 16;
+  const long long e = o / mat_bytes, rem = o % mat_bytes;
+  const int BLK = 16 * SB, LB = SB / 4;
+  const long long bidx = rem / BLK;
+  const int w = (int)(rem % BLK);
+  const int steps = row_bytes / SB;
+  const long long rb = bidx / steps;
+  const int st = (int)(bidx % steps);
+  const int lane = w / LB, j = w % LB;
+  const long long row = rb * 16 + (lane & 15);
+  const long long kb = (long long)st * SB + (lane >> 4) * LB + j;
+  st16(dst + o, ld16(src + e * mat_bytes + row * row_bytes + kb));
+}
+
+hipError_t launch_pack(const void* src, void* dst, int E, int rows, int cols, int fp8,
+                       hipStream_t st) {
+  const int esz = fp8 ? 1 : 2;
+  const long long mat = (long long)rows * cols * esz;
+  const long long chunks = (long long)E * mat / 16;
+  const long long blocks = (chunks + 255) / 256;
+  pack_kernel<<<(unsigned)blocks, 256, 0, st>>>((const uint8_t*)src, (uint8_t*)dst, chunks, mat,
+                                                cols * esz, fp8 ? 128 : 64);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ struct Shape {
   float rsf;
   int x_f32;   // 1: x/out fp32, 0: bf16
   int w_fp8;   // 1: fp8 e4m3 weights with per-row scales
+  int w_packed;  // 1: weights in the MFMA fragment layout
 };
 
 // Byte offsets of each workspace region (all 256-byte aligned).
@@ -62,6 +63,8 @@ struct GemmArgs {
 
 hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st);
 hipError_t launch_down(const Shape& s, const GemmArgs& g, hipStream_t st);
+hipError_t launch_pack(const void* src, void* dst, int E, int rows, int cols, int fp8,
+                       hipStream_t st);
 hipError_t launch_combine(const void* y, const int32_t* inv, int T, int k, int H, int out_f32,
                           void* out, hipStream_t st);
 hipError_t launch_quant_x(const void* x, int x_f32, int T, int H, int k, uint8_t* xq, float* xs,

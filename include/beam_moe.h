@@ -21,9 +21,9 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are device memory owned by the caller, contiguous,
- *     row-major, 16-byte aligned. The library allocates nothing, frees
- *     nothing, and keeps no state between calls other than cached device
- *     properties.
+ *     row-major, 16-byte aligned. The library allocates no device memory and
+ *     keeps no state between calls (the optional stage timing below keeps
+ *     its HIP events until beam_moe_profile_end).
  *   - Calls are asynchronous: they validate their arguments on the host,
  *     enqueue kernels on `stream` (a hipStream_t; NULL = the default stream)
  *     and return. Outputs are valid once the stream has reached that point.
@@ -78,7 +78,8 @@ typedef enum beam_dtype {
  *   hidden and intermediate positive multiples of 128, each <= 65536;
  *   routed_scaling_factor finite;
  *   x_dtype in {BEAM_F32, BEAM_BF16} (the output has the same dtype);
- *   w_dtype in {BEAM_BF16, BEAM_FP8_E4M3}.
+ *   w_dtype in {BEAM_BF16, BEAM_FP8_E4M3};
+ *   w_layout in {BEAM_LAYOUT_ROW_MAJOR, BEAM_LAYOUT_PACKED}.
  */
 typedef struct beam_moe_config {
   int32_t hidden;
@@ -88,9 +89,30 @@ typedef struct beam_moe_config {
   int32_t topk_group;
   int32_t top_k;
   float routed_scaling_factor;
-  int32_t x_dtype; /* beam_dtype */
-  int32_t w_dtype; /* beam_dtype */
+  int32_t x_dtype;  /* beam_dtype */
+  int32_t w_dtype;  /* beam_dtype */
+  int32_t w_layout; /* beam_layout of w_gate, w_up, w_down */
 } beam_moe_config;
+
+/*
+ * Storage layout of the expert weight matrices. Each expert's matrix has R
+ * rows (output channels) and C columns (the reduction): w_gate and w_up
+ * R = intermediate, C = hidden; w_down R = hidden, C = intermediate.
+ *   BEAM_LAYOUT_ROW_MAJOR: element (r, c) at r * C + c ([out, in] row-major).
+ *   BEAM_LAYOUT_PACKED: the MI355X matrix-core fragment layout, made from the
+ *     row-major one by beam_moe_pack_weights. With S = 32 (bf16) or 128
+ *     (fp8) and L = S / 4, element (r, c) is at
+ *       ((r / 16) * (C / S) + c / S) * 16 * S
+ *         + ((r % 16) + 16 * ((c % S) / L)) * L + c % L,
+ *     so that each 16-row by S-column operand of one matrix-core step is one
+ *     contiguous block (1 KB bf16, 2 KB fp8) in the order the 64 lanes of a
+ *     wavefront consume it. Same size as row-major; the per-row fp8 scales
+ *     keep their [n_experts, R] layout.
+ */
+typedef enum beam_layout {
+  BEAM_LAYOUT_ROW_MAJOR = 0,
+  BEAM_LAYOUT_PACKED = 1
+} beam_layout;
 
 /*
  * Bytes of device workspace that beam_moe_route and beam_moe_forward need for
@@ -151,8 +173,57 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
                              float* router_logits_out, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * Convert n_experts row-major [rows, cols] weight matrices (w_dtype BEAM_BF16
+ * or BEAM_FP8_E4M3) at `src` into BEAM_LAYOUT_PACKED at `dst` (same byte
+ * size), on `stream`. A one-time transform at weight-load time: the packed
+ * layout lets every matrix-core operand load of the expert GEMMs read one
+ * contiguous block. src and dst are caller-owned device memory, 16-byte
+ * aligned, and must not overlap.
+ * Errors: BEAM_ERR_NULL (src or dst NULL), BEAM_ERR_SHAPE (n_experts < 1,
+ * rows not a positive multiple of 16, cols not a positive multiple of 128,
+ * or more than 2^40 bytes in all), BEAM_ERR_DTYPE, BEAM_ERR_ALIGN,
+ * BEAM_ERR_HIP (launch failed).
+ */
+beam_status beam_moe_pack_weights(const void* src, void* dst, int32_t n_experts, int32_t rows,
+                                  int32_t cols, int32_t w_dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* beam_moe_status_string(int32_t status);
+
+/*
+ * Stage timing. The kernels of one call, in launch order (forward: all that
+ * apply to its dtypes; route: the first two, plus the histogram and scan when
+ * counts are requested).
+ */
+typedef enum beam_stage {
+  BEAM_STAGE_ROUTER_LOGITS = 0, /* fp32 router logits */
+  BEAM_STAGE_SELECT = 1,        /* sigmoid, bias, group top-2, kept groups, top-k, normalise */
+  BEAM_STAGE_PERM_HIST = 2,     /* per-chunk expert histogram */
+  BEAM_STAGE_PERM_SCAN = 3,     /* counts, offsets, GEMM tile list */
+  BEAM_STAGE_PERM_SCATTER = 4,  /* stable scatter into expert order */
+  BEAM_STAGE_QUANT_X = 5,       /* fp8 weights only: per-token E4M3 quantisation of x */
+  BEAM_STAGE_GATEUP = 6,        /* grouped gate/up GEMM + SwiGLU */
+  BEAM_STAGE_QUANT_H = 7,       /* fp8 weights only: per-row E4M3 quantisation of h */
+  BEAM_STAGE_DOWN = 8,          /* grouped down GEMM, scaled by rsf * weight */
+  BEAM_STAGE_COMBINE = 9,       /* weighted combine into the output */
+  BEAM_STAGE_COUNT = 10
+} beam_stage;
+
+/*
+ * beam_moe_profile_begin(mask): from now on, every route/forward call in the
+ * process records a pair of HIP timing events around the launch of each
+ * stage s with bit (1 << s) set in `mask`, on the call's stream. Clears
+ * earlier records. The library creates the events (no device memory).
+ * beam_moe_profile_end(total_ms, launches): waits for the recorded events,
+ * writes for every stage s < BEAM_STAGE_COUNT the summed elapsed
+ * milliseconds total_ms[s] and the number of timed launches launches[s]
+ * (either pointer may be NULL), releases the events and stops recording.
+ * Both return BEAM_ERR_HIP if a HIP event call fails. Meant for measurement
+ * runs; the events add a few microseconds per timed launch.
+ */
+beam_status beam_moe_profile_begin(uint32_t stage_mask);
+beam_status beam_moe_profile_end(float* total_ms, int32_t* launches);
 
 #ifdef __cplusplus
 }

@@ -29,11 +29,21 @@ def f64(t):
     return t.detach().to("cpu", torch.float64).numpy() if t.dtype != torch.float8_e4m3fn else None
 
 
+def packed_copy(w):
+    """The same weights in the MFMA fragment layout (made by the library)."""
+    pw = dict(w)
+    for k in ("w_gate", "w_up", "w_down"):
+        pw[k] = gl.pack_weights(w[k])
+    pw["packed"] = True
+    return pw
+
+
 def run_forward(x, rw, b, w, cfg, **kw):
     scales = None
     if w["w_gate"].dtype == torch.float8_e4m3fn:
         scales = (w["w_gate_scale"], w["w_up_scale"], w["w_down_scale"])
     out, r = gl.forward(x, rw, b, w["w_gate"], w["w_up"], w["w_down"], scales=scales,
+                        packed=w.get("packed", False),
                         n_group=cfg["n_group"], topk_group=cfg["topk_group"], top_k=cfg["top_k"],
                         routed_scaling_factor=cfg["routed_scaling_factor"], return_routing=True,
                         return_logits=True, **kw)

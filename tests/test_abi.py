@@ -130,3 +130,15 @@ def test_workspace_size(L):
     assert gl.workspace_bytes(beam_cfg(n_group=3), 64) == 0
     f8 = gl.workspace_bytes(beam_cfg(w_dtype=gl.BEAM_FP8_E4M3), 64)
     assert f8 > 0
+
+
+def test_layout_and_pack_checks(L):
+    assert _fwd(L, beam_cfg(w_layout=2), 8) == gl.BEAM_ERR_CONFIG
+    v = ctypes.c_void_p
+    pk = L.beam_moe_pack_weights
+    assert pk(None, v(FAKE), 256, 2560, 5120, gl.BEAM_BF16, None) == gl.BEAM_ERR_NULL
+    assert pk(v(FAKE), v(FAKE), 256, 2560, 5120, gl.BEAM_F32, None) == gl.BEAM_ERR_DTYPE
+    for E, R, C in [(0, 2560, 5120), (256, 2568, 5120), (256, 2560, 5000), (256, 0, 5120),
+                    (1 << 20, 2560, 5120)]:
+        assert pk(v(FAKE), v(FAKE), E, R, C, gl.BEAM_BF16, None) == gl.BEAM_ERR_SHAPE, (E, R, C)
+    assert pk(v(FAKE + 8), v(FAKE), 256, 2560, 5120, gl.BEAM_BF16, None) == gl.BEAM_ERR_ALIGN

@@ -21,7 +21,7 @@ import oracle
 import workloads
 import group_limited_routing_amd as gl
 from parity import (check_logits, check_outputs, check_routing, oracle_reference, run_forward,
-                    output_errors)
+                    output_errors, packed_copy)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,11 +48,12 @@ def _report(name, rep):
     print(f"\n[parity] {name}: " + json.dumps(rep), flush=True)
 
 
-def _full_compare(name, cfg, seed=0):
-    """Every token against the oracle."""
+def _full_compare(name, cfg, seed=0, packed=False):
+    """Every token against the oracle (the oracle always reads the row-major
+    weights; the GPU optionally their packed copy)."""
     dev = _dev()
     x, rw, b, w = _inputs(cfg, seed, dev)
-    out, r = run_forward(x, rw, b, w, cfg)
+    out, r = run_forward(x, rw, b, packed_copy(w) if packed else w, cfg)
     x64 = x.cpu().double().numpy()
     rw64 = rw.cpu().double().numpy()
     ora = oracle.route(x64, rw64, b.cpu().double().numpy(), cfg["n_group"], cfg["topk_group"],
@@ -74,29 +75,60 @@ def test_tiny_workload(seed):
     _full_compare(f"tiny seed {seed}", cfg, seed)
 
 
-def test_ragged_stream_variant():
+LAYOUTS = [pytest.param(False, id="rowmajor"), pytest.param(True, id="packed")]
+
+
+@pytest.mark.parametrize("packed", LAYOUTS)
+def test_ragged_stream_variant(packed):
     cfg = _case(300, 384, 256)          # 2400 pairs: streaming GEMMs; H % 256 != 0
-    _full_compare("ragged stream", cfg, 3)
+    _full_compare("ragged stream", cfg, 3, packed)
 
 
-def test_ragged_tiled_variant():
+@pytest.mark.parametrize("packed", LAYOUTS)
+def test_stream_variant_wide(packed):
+    cfg = _case(150, 1024, 512)         # widths that take the 8-fragment waves
+    _full_compare("stream wide", cfg, 13, packed)
+
+
+@pytest.mark.parametrize("packed", LAYOUTS)
+def test_ragged_tiled_variant(packed):
     cfg = _case(1000, 512, 384)         # 8000 pairs: LDS-tiled GEMMs, ragged tiles
-    _full_compare("ragged tiled", cfg, 4)
+    _full_compare("ragged tiled", cfg, 4, packed)
 
 
-def test_fp32_x_tiled_variant():
+@pytest.mark.parametrize("packed", LAYOUTS)
+def test_fp32_x_tiled_variant(packed):
     cfg = _case(700, 256, 128, x_dtype="f32")
-    _full_compare("fp32 x tiled", cfg, 5)
+    _full_compare("fp32 x tiled", cfg, 5, packed)
 
 
-def test_fp8_stream_variant():
+@pytest.mark.parametrize("packed", LAYOUTS)
+def test_fp8_stream_variant(packed):
     cfg = _case(200, 512, 256, w_dtype="fp8")
-    _full_compare("fp8 stream", cfg, 6)
+    _full_compare("fp8 stream", cfg, 6, packed)
 
 
-def test_fp8_tiled_variant():
+@pytest.mark.parametrize("packed", LAYOUTS)
+def test_fp8_tiled_variant(packed):
     cfg = _case(900, 384, 256, w_dtype="fp8")
-    _full_compare("fp8 tiled", cfg, 7)
+    _full_compare("fp8 tiled", cfg, 7, packed)
+
+
+@pytest.mark.parametrize("dtype,S", [(torch.bfloat16, 32), (torch.float8_e4m3fn, 128)])
+def test_pack_layout_matches_definition(dtype, S):
+    """The packed copy equals the documented layout, built here with a torch
+    view/permute of the row-major tensor (an independent formulation)."""
+    dev = _dev()
+    E, R, C = 3, 48, 384
+    g = torch.Generator(device=dev).manual_seed(1)
+    w = torch.randn((E, R, C), generator=g, device=dev).to(dtype)
+    p = gl.pack_weights(w)
+    torch.cuda.synchronize()
+    L = S // 4
+    ref = w.view(torch.uint8 if dtype != torch.bfloat16 else torch.int16)
+    ref = ref.view(E, R // 16, 16, C // S, 4, L).permute(0, 1, 3, 4, 2, 5).contiguous().view(E, R, C)
+    got = p.view(ref.dtype)
+    assert torch.equal(got, ref)
 
 
 @pytest.mark.parametrize("n_group,topk_group,top_k", [(1, 1, 8), (8, 8, 8), (64, 16, 8), (8, 4, 1),
@@ -180,12 +212,13 @@ def _sample_tokens(r, near, T, hot=None, n=4):
     return np.array(sorted(set(int(t) for t in toks)))
 
 
-def _full_shape(name, wl, w, extra=None):
+def _full_shape(name, wl, w, extra=None, oracle_weights=None):
     dev = _dev()
     cfg = workloads.workload(wl)
     x, rw, b = workloads.make_small_inputs(cfg, 0)
     x, rw, b = x.to(dev), rw.to(dev), b.to(dev)
     out, r = run_forward(x, rw, b, w, cfg)
+    w = oracle_weights if oracle_weights is not None else w
     x64 = x.cpu().double().numpy()
     rw64 = rw.cpu().double().numpy()
     ora = oracle.route(x64, rw64, b.cpu().double().numpy(), 8, 4, 8)
@@ -205,6 +238,16 @@ def _full_shape(name, wl, w, extra=None):
 
 def test_beam_decode_full_shape(beam_bf16_weights):
     _full_shape("decode T=64", "decode", beam_bf16_weights)
+
+
+def test_beam_decode_full_shape_packed(beam_bf16_weights):
+    pw = packed_copy(beam_bf16_weights)
+    torch.cuda.synchronize()
+    try:
+        _full_shape("decode T=64 packed", "decode", pw, oracle_weights=beam_bf16_weights)
+    finally:
+        del pw
+        torch.cuda.empty_cache()
 
 
 def test_beam_prefill_full_shape(beam_bf16_weights):

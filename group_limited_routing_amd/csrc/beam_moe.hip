@@ -37,6 +37,8 @@ Layout make_layout(const Shape& s) {
   L.meta = take(64 * 4);
   L.tile_e = take((size_t)L.max_mtiles * 4);
   L.tile_r = take((size_t)L.max_mtiles * 4);
+  L.e_tstart = take(E * 4);
+  L.e_ntiles = take(E * 4);
   L.stok = take(P * 4);
   L.sw = take(P * 4);
   L.inv = take(P * 4);
@@ -165,7 +167,8 @@ struct Buffers {
   float* z;
   int32_t* idx;
   float* w;
-  int32_t *chist, *cbase, *counts, *offsets, *meta, *tile_e, *tile_r, *stok, *inv;
+  int32_t *chist, *cbase, *counts, *offsets, *meta, *tile_e, *tile_r, *e_tstart, *e_ntiles, *stok,
+      *inv;
   float* sw;
 };
 
@@ -182,6 +185,8 @@ Buffers carve(const Layout& L, void* ws) {
   B.meta = (int32_t*)(b + L.meta);
   B.tile_e = (int32_t*)(b + L.tile_e);
   B.tile_r = (int32_t*)(b + L.tile_r);
+  B.e_tstart = (int32_t*)(b + L.e_tstart);
+  B.e_ntiles = (int32_t*)(b + L.e_ntiles);
   B.stok = (int32_t*)(b + L.stok);
   B.sw = (float*)(b + L.sw);
   B.inv = (int32_t*)(b + L.inv);
@@ -237,7 +242,8 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
   if (expert_counts) {
     STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(topk_idx, T, s.top_k, B.chist, st));
     STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, kTiledBM, B.cbase, B.counts, B.offsets,
-                                 B.meta, B.tile_e, B.tile_r, expert_counts, st));
+                                 B.meta, B.tile_e, B.tile_r, B.e_tstart, B.e_ntiles,
+                                 expert_counts, st));
   }
   return BEAM_OK;
 }
@@ -274,18 +280,20 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
   int32_t* idx = topk_idx_out ? topk_idx_out : B.idx;
   float* w = topk_w_out ? topk_w_out : B.w;
   const int k = s.top_k;
-  const int BM = use_stream_gemm(s) ? kStreamBM : kTiledBM;
+  const int BM = use_stream_gemm(s) ? kStreamBM : (s.w_packed ? wide_bm(s) : kTiledBM);
 
   STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
   STAGE(BEAM_STAGE_SELECT, launch_select(z, expert_bias, T, s.n_group, s.topk_group, k, idx, w, st));
   STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(idx, T, k, B.chist, st));
   STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts, B.offsets, B.meta,
-                               B.tile_e, B.tile_r, expert_counts_out, st));
+                               B.tile_e, B.tile_r, B.e_tstart, B.e_ntiles, expert_counts_out, st));
   STAGE(BEAM_STAGE_PERM_SCATTER, launch_perm_scatter(idx, w, T, k, s.rsf, B.cbase, B.offsets, B.stok, B.sw, B.inv, st));
 
   GemmArgs g{};
   g.tile_e = B.tile_e;
   g.tile_r = B.tile_r;
+  g.e_tstart = B.e_tstart;
+  g.e_ntiles = B.e_ntiles;
   g.meta = B.meta;
   g.offsets = B.offsets;
   g.stok = B.stok;

@@ -85,6 +85,39 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sign | (code > 0x7eu ? 0x7eu : code);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes lds_base + 16 l (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+#endif
+}
+
+// Wait until at most N vector-memory operations of this wave are pending
+// (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+#endif
+}
+
+// Wait until all LDS/scalar-memory operations of this wave have completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+#endif
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (the fence
+// would wait for every pending global->LDS load, not just the needed ones).
+__device__ __forceinline__ void barrier_only() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_barrier();
+#endif
+}
+
 __device__ __forceinline__ float sigmoid_f32(float z) {
   return 1.0f / (1.0f + expf(-z));
 }

@@ -495,6 +495,365 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
   }
 }
 
+// Epilogue of the transposed tiles (wide and DMA variants). acc[fm][fn]
+// holds, in lane (r, g), output row row_base + 16 fm + r and the 4 output
+// columns 16 c(fn) + 4 g .. + 3, where c(fn) is the fragment's column block:
+// gate/up: fn = 0, 1 gate and fn + 2 the matching up block, c = 2 wn + fn;
+// down: c = 4 wn + fn.
+template <int MODE, bool FP8, int FM, int FN>
+__device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const TileInfo& ti,
+                                                    const f32x4 (&acc)[FM][FN], int row_base,
+                                                    int n0, int wn, int r, int g) {
+  const int N = p.N;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int row = row_base + fm * 16 + r;
+    const bool valid = row < ti.rows;
+    const size_t orow = (size_t)(ti.row0 + (valid ? row : 0)) * N;
+    if (MODE == 0) {
+      float rowmax = 0.f;
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn) {
+        const int n = n0 + (wn * 2 + fn) * 16 + 4 * g;
+        float h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[i] = valid ? gateup_value<FP8>(p, ti, row, n + i, acc[fm][fn][i], acc[fm][fn + 2][i]) : 0.f;
+          rowmax = fmaxf(rowmax, fabsf(h[i]));
+        }
+        if (valid) {
+          if constexpr (FP8)
+            st16((float*)p.out + orow + n, u32x4{__float_as_uint(h[0]), __float_as_uint(h[1]),
+                                                 __float_as_uint(h[2]), __float_as_uint(h[3])});
+          else
+            *reinterpret_cast<u32x2*>((uint16_t*)p.out + orow + n) =
+                u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+        }
+      }
+      if constexpr (FP8) {
+        // the row's 32 columns of this wave sit in lanes r, r + 16, r + 32, r + 48
+        rowmax = fmaxf(rowmax, __shfl_xor(rowmax, 16));
+        rowmax = fmaxf(rowmax, __shfl_xor(rowmax, 32));
+        if (valid && g == 0) atomicMax(&p.hamax[ti.row0 + row], __float_as_uint(rowmax));
+      }
+    } else {
+      if (valid) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int n = n0 + (wn * 4 + fn) * 16 + 4 * g;
+          float y[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] = down_value<FP8>(p, ti, row, n + i, acc[fm][fn][i]);
+          *reinterpret_cast<u32x2*>((uint16_t*)p.out + orow + n) =
+              u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        }
+      }
+    }
+  }
+}
+
+// M-tiles per ordering group of the wide and DMA variants: the 32 blocks that
+// run together on one XCD cover 4 M-tiles x 8 N-tiles of an expert, so each
+// A slice is shared by 8 of them and each weight slice by 4 in the XCD's L2.
+constexpr int kGroupM = 4;
+
+// ---------------------------------------------------------------- wide variant
+// Prefill with packed weights. A workgroup of 8 waves (two per SIMD) computes
+// BM rows x 256 weight rows (gate/up: 128 gate + 128 up columns; down: 256
+// columns) over K in stages of 128 bytes of k, double buffered in LDS (A
+// swizzled row-major, B as the packed fragment blocks read back in lane
+// order). Waves form a 2 x 4 grid: BM = 256 -> 128 x 64 per wave (32
+// fragments), BM = 128 -> 64 x 64 (16 fragments). Every k-step loads all of a
+// wave's operand fragments before its MFMAs; the second wave on the SIMD
+// covers the LDS latency.
+//
+// Tile order: the active (M-tile, N-tile) pairs are numbered expert by
+// expert, in blocks of kGroupM M-tiles, N-tile-major inside a block; block b
+// takes number start(b % 8) + b / 8, where XCD x = b % 8 owns a contiguous
+// share, so blocks running together on one XCD share A and weight slices in
+// that XCD's L2.
+//
+// The MFMAs compute the transposed tile (weight fragment as the A operand):
+// each lane then holds 4 consecutive output columns of one row, stored as
+// one 8-byte (bf16) or 16-byte (fp32) write.
+template <int MODE, typename AT, bool FP8, int BM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_wide_kernel(GemmArgs p) {
+  using WT = typename WTraits<FP8>::W;
+  constexpr int BK = FP8 ? 128 : 64;          // k values per stage (128 bytes per row)
+  constexpr int CH = BK / 8;                  // values per 16-byte chunk
+  constexpr int A_BYTES = BM * 128, B_BYTES = 256 * 128, STAGE = A_BYTES + B_BYTES;
+  constexpr int FM = BM / 32, FN = 4;         // fragments per wave along M / N
+  constexpr int COLS = (MODE == 0) ? 128 : 256;
+  constexpr int AQ = BM / 64;                 // A chunks per thread per stage
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int ntn = p.N / COLS;
+  const int n_tiles = p.meta[0] * ntn;
+  const int b = blockIdx.x;
+  if (b >= n_tiles) return;
+  // XCD-contiguous numbering of the active tiles
+  const int xcd = b & 7, per = n_tiles >> 3, extra = n_tiles & 7;
+  const int j = xcd * per + min(xcd, extra) + (b >> 3);
+  const int e = p.tile_e[j / ntn];
+  const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
+  const int jj = j - ts * ntn;
+  // inside the expert: blocks of kGroupM M-tiles, N-tile-major inside a block
+  const int mb = jj / (kGroupM * ntn), rem = jj - mb * kGroupM * ntn;
+  const int gm = min(kGroupM, nm - mb * kGroupM);
+  const int nt = rem / gm, mt = ts + mb * kGroupM + rem % gm;
+  TileInfo ti;
+  ti.e = e;
+  ti.row0 = p.tile_r[mt];
+  ti.rows = min(BM, p.offsets[e + 1] - ti.row0);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3, r = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N;
+  const int n0 = nt * COLS;
+
+  // A: AQ chunks per thread; chunk q = tid + 512 i -> tile row q / 8, chunk q % 8.
+  const AT* agp[AQ];
+  int aoff[AQ];
+#pragma unroll
+  for (int i = 0; i < AQ; ++i) {
+    const int q = tid + 512 * i, lr = q >> 3, c = q & 7;
+    const int ar = min(lr, ti.rows - 1);
+    agp[i] = (MODE == 0) ? (const AT*)p.a + (size_t)p.stok[ti.row0 + ar] * K + c * CH
+                         : (const AT*)p.a + (size_t)(ti.row0 + ar) * K + c * CH;
+    aoff[i] = swz(lr, c);
+  }
+  // B: 4 chunks per thread; chunk q = tid + 512 i -> row block q / 128 of the
+  // tile (16 blocks; MODE 0: gate 0..7 then up 8..15), 16 bytes (q % 128) of
+  // its stage block. Row block of chunk i: (tid >> 7) + 4 i.
+  const WT* bgp[4];
+  {
+    const size_t eoff = (size_t)ti.e * N * K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rbk = (tid >> 7) + 4 * i;
+      const WT* W = (const WT*)((MODE == 0 && rbk >= 8) ? p.w1 : p.w0);
+      const int blk = (MODE == 0) ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
+      bgp[i] = W + eoff + (size_t)blk * 16 * K + (tid & 127) * CH;
+    }
+  }
+
+  int arow_l[FM], brbl[FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f) arow_l[f] = wm * (BM / 2) + f * 16 + r;
+#pragma unroll
+  for (int f = 0; f < FN; ++f)
+    brbl[f] = (MODE == 0) ? ((f < 2) ? wn * 2 + f : 8 + wn * 2 + (f - 2)) : wn * 4 + f;
+  // Waves whose rows are all padding skip their MFMAs (uniform per wave).
+  const bool live = wm * (BM / 2) < ti.rows;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  using AL = typename std::conditional<FP8, ALoad16<uint16_t>, ALoad16<AT>>::type;
+  AL ra[AQ];
+  u32x4 rb[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < AQ; ++i) {
+      if constexpr (FP8)
+        ra[i].v = ld16(agp[i] + (size_t)kt * BK);
+      else
+        ra[i].load(agp[i] + (size_t)kt * BK);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb[i] = ld16(bgp[i] + (size_t)kt * 16 * BK);
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* base = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < AQ; ++i) st16(base + aoff[i], ra[i].bits());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st16(base + A_BYTES + ((tid >> 7) + 4 * i) * 2048 + (tid & 127) * 16, rb[i]);
+  };
+
+  const int nk = K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint8_t* As = smem + buf * STAGE;
+    const uint8_t* Bs = As + A_BYTES;
+    if (live) {
+      if constexpr (FP8) {
+        Op32 af[FM], bfr[FN];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const uint8_t* blk = Bs + brbl[f] * 2048 + lane * 32;
+          bfr[f].lo = ld16(blk);
+          bfr[f].hi = ld16(blk + 16);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          af[i].lo = ld16(As + swz(arow_l[i], 2 * g));
+          af[i].hi = ld16(As + swz(arow_l[i], 2 * g + 1));
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_op(bfr[jn], af[i], acc[i][jn]);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          u32x4 af[FM], bfr[FN];
+#pragma unroll
+          for (int f = 0; f < FN; ++f) bfr[f] = ld16(Bs + (brbl[f] * 2 + s) * 1024 + lane * 16);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) af[i] = ld16(As + swz(arow_l[i], s * 4 + g));
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_op(bfr[jn], af[i], acc[i][jn]);
+        }
+      }
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  transposed_epilogue<MODE, FP8, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
+}
+
+// ---------------------------------------------------------------- DMA variant
+// Prefill with packed bf16 weights and bf16 A. Same tile shape, wave grid and
+// tile order as the wide variant, but operands go from global memory straight
+// into LDS (global_load_lds, 16 bytes per lane, no staging registers) through
+// a ring of NS stages of one 32-k matrix-core step each, filled NS-1 stages
+// ahead, so roughly three stages of loads are in flight while one is
+// computed. Waits are explicit: before stage kt is read, vmcnt leaves only
+// the DMAs of the later stages outstanding, and a raw barrier publishes every
+// wave's stage-kt DMAs. Each wave consumes its LDS reads (its MFMAs need
+// them) before the barrier that lets a stage buffer be refilled.
+//
+// LDS per stage: A is BM rows x 64 bytes, row r's chunk g (16 bytes) stored at
+// position g ^ ((r >> 1) & 3) so the 16 rows of a fragment read hit distinct
+// banks; B is 16 row blocks x 1 KB in the packed fragment order.
+
+template <int MODE, int BM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_dma_kernel(GemmArgs p) {
+  constexpr int NS = 4;                        // stages in the ring
+  constexpr int A_BYTES = BM * 64, B_BYTES = 256 * 64, STAGE = A_BYTES + B_BYTES;
+  constexpr int FM = BM / 32, FN = 4;
+  constexpr int COLS = (MODE == 0) ? 128 : 256;
+  constexpr int AI = BM / 128;                 // A DMA instructions per wave per stage
+  constexpr int PER_STAGE = AI + 2;            // DMA instructions per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const int ntn = p.N / COLS;
+  const int n_tiles = p.meta[0] * ntn;
+  const int b = blockIdx.x;
+  if (b >= n_tiles) return;
+  const int xcd = b & 7, per = n_tiles >> 3, extra = n_tiles & 7;
+  const int j = xcd * per + min(xcd, extra) + (b >> 3);
+  const int e = p.tile_e[j / ntn];
+  const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
+  const int jj = j - ts * ntn;
+  // inside the expert: blocks of kGroupM M-tiles, N-tile-major inside a block
+  const int mb = jj / (kGroupM * ntn), rem = jj - mb * kGroupM * ntn;
+  const int gm = min(kGroupM, nm - mb * kGroupM);
+  const int nt = rem / gm, mt = ts + mb * kGroupM + rem % gm;
+  TileInfo ti;
+  ti.e = e;
+  ti.row0 = p.tile_r[mt];
+  ti.rows = min(BM, p.offsets[e + 1] - ti.row0);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3, r = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N;
+  const int n0 = nt * COLS;
+
+  // A DMA sources: instruction i of this wave fills tile rows 16 * (wave * AI + i) ..;
+  // lane l writes LDS row l / 4, position l % 4, which holds chunk (l % 4) ^ ((row >> 1) & 3).
+  const uint16_t* asrc[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = (wave * AI + i) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    const int ar = min(row, ti.rows - 1);
+    const uint16_t* base = (MODE == 0) ? (const uint16_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K
+                                       : (const uint16_t*)p.a + (size_t)(ti.row0 + ar) * K;
+    asrc[i] = base + chunk * 8;
+  }
+  // B DMA sources: instruction i fills row block wave * 2 + i (MODE 0: 0..7 gate, 8..15 up).
+  const uint16_t* bsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rbk = wave * 2 + i;
+    const uint16_t* W = (const uint16_t*)((MODE == 0 && rbk >= 8) ? p.w1 : p.w0);
+    const int blk = (MODE == 0) ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
+    bsrc[i] = W + (size_t)ti.e * N * K + (size_t)blk * 16 * K + lane * 8;
+  }
+  auto issue = [&](int kt) {  // DMA of k-step kt into ring slot kt % NS
+    uint8_t* st = smem + (kt % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      dma16(asrc[i] + (size_t)kt * 32, st + (wave * AI + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma16(bsrc[i] + (size_t)kt * 512, st + A_BYTES + (wave * 2 + i) * 1024);
+  };
+
+  int aoff[FM], boff[FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f) {
+    const int row = wm * (BM / 2) + f * 16 + r;
+    aoff[f] = row * 64 + ((g ^ ((row >> 1) & 3)) << 4);
+  }
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const int rbl = (MODE == 0) ? ((f < 2) ? wn * 2 + f : 8 + wn * 2 + (f - 2)) : wn * 4 + f;
+    boff[f] = A_BYTES + rbl * 1024 + lane * 16;
+  }
+  const bool live = wm * (BM / 2) < ti.rows;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / 32;  // >= 4 since K is a multiple of 128
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt done for this wave: at most the later issued stages outstanding
+    if (kt + NS - 2 < nk)
+      wait_vmcnt<(NS - 2) * PER_STAGE>();
+    else
+      wait_vmcnt<0>();
+    barrier_only();  // ... and for every wave; all reads of kt - 1 retired
+    asm volatile("" ::: "memory");
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);  // refills the slot read at kt - 1
+    if (live) {
+      const uint8_t* st = smem + (kt % NS) * STAGE;
+      u32x4 af[FM], bfr[FN];
+#pragma unroll
+      for (int f = 0; f < FN; ++f) bfr[f] = ld16(st + boff[f]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = ld16(st + aoff[i]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_op(bfr[jn], af[i], acc[i][jn]);
+    }
+    wait_lgkmcnt0();
+    asm volatile("" ::: "memory");
+  }
+
+  transposed_epilogue<MODE, false, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
+}
+
 // ---------------------------------------------------------------- launchers
 int mtile_bound(const Shape& s, int BM) {
   const long long pairs = (long long)s.T * s.top_k;
@@ -530,13 +889,40 @@ static void launch_tiled(const Shape& s, const GemmArgs& g, hipStream_t st) {
   gemm_tiled_kernel<MODE, AT, FP8, PACKED><<<grid, 256, 0, st>>>(g);
 }
 
+int wide_bm(const Shape& s) {
+  // 256-row tiles once experts average 192 rows or more
+  return (long long)s.T * s.top_k >= 192LL * s.E ? 256 : 128;
+}
+
+template <int MODE, typename AT, bool FP8, int BM>
+static void launch_wide_bm(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  // The grid is a bound on the active tile count, rounded up to a multiple of
+  // the 8 XCDs; blocks past the active count exit at once.
+  long long n = (long long)mtile_bound(s, BM) * (g.N / (MODE == 0 ? 128 : 256));
+  n = (n + 7) & ~7LL;
+  if constexpr (!FP8 && std::is_same<AT, uint16_t>::value)
+    gemm_dma_kernel<MODE, BM><<<(unsigned)n, 512, 0, st>>>(g);
+  else
+    gemm_wide_kernel<MODE, AT, FP8, BM><<<(unsigned)n, 512, 0, st>>>(g);
+}
+
+template <int MODE, typename AT, bool FP8>
+static void launch_wide(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  if (wide_bm(s) == 256)
+    launch_wide_bm<MODE, AT, FP8, 256>(s, g, st);
+  else
+    launch_wide_bm<MODE, AT, FP8, 128>(s, g, st);
+}
+
 template <int MODE, typename AT, bool FP8>
 static void launch_variant(const Shape& s, const GemmArgs& g, hipStream_t st) {
   const bool stream = use_stream_gemm(s);
   if (s.w_packed) {
     if (stream)
       launch_stream<MODE, AT, FP8, true>(s, g, st);
-    else
+    else if (g.N % (MODE == 0 ? 128 : 256) == 0)
+      launch_wide<MODE, AT, FP8>(s, g, st);
+    else  // down pass with hidden not a multiple of 256: 128-column tiles
       launch_tiled<MODE, AT, FP8, true>(s, g, st);
   } else {
     if (stream)

@@ -9,7 +9,7 @@ namespace beam {
 
 // Row tile (tokens per M-tile) of the two expert-GEMM variants.
 constexpr int kStreamBM = 16;   // decode: weight streaming, one MFMA row block
-constexpr int kTiledBM = 128;   // prefill: LDS-staged MFMA tiles
+constexpr int kTiledBM = 128;   // prefill, row-major weights: LDS-staged MFMA tiles
 
 struct Shape {
   int T, H, I, E, n_group, topk_group, top_k;
@@ -21,13 +21,15 @@ struct Shape {
 
 // Byte offsets of each workspace region (all 256-byte aligned).
 struct Layout {
-  size_t z, idx, w, chist, cbase, counts, offsets, meta, tile_e, tile_r;
+  size_t z, idx, w, chist, cbase, counts, offsets, meta, tile_e, tile_r, e_tstart, e_ntiles;
   size_t stok, sw, inv, xq, xs, hamax, h, hq, hs, y, total;
   int nchunks, max_mtiles;
 };
 
 Layout make_layout(const Shape& s);
 bool use_stream_gemm(const Shape& s);
+// prefill with packed weights: M-tile of 128 or 256 rows, from the rows per expert
+int wide_bm(const Shape& s);
 int mtile_bound(const Shape& s, int BM);
 
 hipError_t launch_router_logits(const void* x, int x_f32, const float* W, float* z, int T, int H,
@@ -37,7 +39,8 @@ hipError_t launch_select(const float* z, const float* bias, int T, int n_group, 
 hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int32_t* chist, hipStream_t st);
 hipError_t launch_perm_scan(const int32_t* chist, int nchunks, int BM, int32_t* cbase,
                             int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,
-                            int32_t* tile_r, int32_t* counts_out, hipStream_t st);
+                            int32_t* tile_r, int32_t* e_tstart, int32_t* e_ntiles,
+                            int32_t* counts_out, hipStream_t st);
 hipError_t launch_perm_scatter(const int32_t* idx, const float* w, int T, int k, float rsf,
                                const int32_t* cbase, const int32_t* offsets, int32_t* stok,
                                float* sw, int32_t* inv, hipStream_t st);
@@ -51,6 +54,8 @@ struct GemmArgs {
   const float* a_scale;     // fp8: per-row activation scales (x: [T], h: [T*k])
   const int32_t* tile_e;
   const int32_t* tile_r;
+  const int32_t* e_tstart;  // first M-tile of each expert
+  const int32_t* e_ntiles;  // M-tiles of each expert
   const int32_t* meta;
   const int32_t* offsets;
   const int32_t* stok;

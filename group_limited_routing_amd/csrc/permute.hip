@@ -65,7 +65,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
 //   cbase[c, e]  = tokens of expert e in chunks before c;
 //   counts[e]    = tokens of expert e; offsets = exclusive scan of counts;
 //   M-tiles of BM rows per expert, listed expert by expert:
-//   tile_e[m] = expert, tile_r[m] = first sorted row; meta[0] = tile count.
+//   tile_e[m] = expert, tile_r[m] = first sorted row; meta[0] = tile count;
+//   e_tstart[e], e_ntiles[e] = first M-tile of expert e and its tile count.
 __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restrict__ chist,
                                                         int nchunks, int BM,
                                                         int32_t* __restrict__ cbase,
@@ -74,6 +75,8 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ meta,
                                                         int32_t* __restrict__ tile_e,
                                                         int32_t* __restrict__ tile_r,
+                                                        int32_t* __restrict__ e_tstart,
+                                                        int32_t* __restrict__ e_ntiles,
                                                         int32_t* __restrict__ counts_out) {
   __shared__ int wsum[4];
   const int e = threadIdx.x;
@@ -90,6 +93,8 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restric
   if (e == kExperts - 1) offsets[kExperts] = off + run;
   const int mt = (run + BM - 1) / BM;
   const int ts = block_exclusive_scan(mt, wsum);
+  e_tstart[e] = ts;
+  e_ntiles[e] = mt;
   for (int i = 0; i < mt; ++i) {
     tile_e[ts + i] = e;
     tile_r[ts + i] = off + i * BM;
@@ -131,9 +136,10 @@ hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int32_t* chist, hi
 
 hipError_t launch_perm_scan(const int32_t* chist, int nchunks, int BM, int32_t* cbase,
                             int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,
-                            int32_t* tile_r, int32_t* counts_out, hipStream_t st) {
+                            int32_t* tile_r, int32_t* e_tstart, int32_t* e_ntiles,
+                            int32_t* counts_out, hipStream_t st) {
   perm_scan_kernel<<<1, 256, 0, st>>>(chist, nchunks, BM, cbase, counts, offsets, meta, tile_e,
-                                      tile_r, counts_out);
+                                      tile_r, e_tstart, e_ntiles, counts_out);
   return hipGetLastError();
 }
 

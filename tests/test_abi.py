@@ -142,3 +142,23 @@ def test_layout_and_pack_checks(L):
                     (1 << 20, 2560, 5120)]:
         assert pk(v(FAKE), v(FAKE), E, R, C, gl.BEAM_BF16, None) == gl.BEAM_ERR_SHAPE, (E, R, C)
     assert pk(v(FAKE + 8), v(FAKE), 256, 2560, 5120, gl.BEAM_BF16, None) == gl.BEAM_ERR_ALIGN
+
+
+def test_library_links_every_kernel(L):
+    """Every kernel launched by the library has its host launch stub in the
+    .so and nothing of the library is left undefined (a kernel whose host-side
+    instantiation fails would otherwise leave a launch that never happens)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    und = subprocess.run([nm, "-DC", "--undefined-only", gl.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert "beam::" not in und, [ln for ln in und.splitlines() if "beam::" in ln]
+    syms = subprocess.run([nm, "-C", gl.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    for kernel in ["router_logits_kernel", "select_kernel", "perm_hist_kernel", "perm_scan_kernel",
+                   "perm_scatter_kernel", "gemm_stream_kernel", "gemm_tiled_kernel",
+                   "gemm_wide_kernel", "gemm_dma_kernel", "combine_kernel", "quant_x_kernel",
+                   "quant_h_kernel", "pack_kernel"]:
+        assert f"__device_stub__{kernel}" in syms, kernel

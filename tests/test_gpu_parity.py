@@ -102,6 +102,11 @@ def test_fp32_x_tiled_variant(packed):
     _full_compare("fp32 x tiled", cfg, 5, packed)
 
 
+def test_wide_variant_256_rows():
+    cfg = _case(6500, 256, 256)         # ~203 rows per expert: 256-row tiles, ragged
+    _full_compare("wide 256", cfg, 14, True)
+
+
 @pytest.mark.parametrize("packed", LAYOUTS)
 def test_fp8_stream_variant(packed):
     cfg = _case(200, 512, 256, w_dtype="fp8")
@@ -240,36 +245,49 @@ def test_beam_decode_full_shape(beam_bf16_weights):
     _full_shape("decode T=64", "decode", beam_bf16_weights)
 
 
-def test_beam_decode_full_shape_packed(beam_bf16_weights):
+def test_beam_decode_full_shape_packed(beam_bf16_weights, beam_bf16_packed):
+    _full_shape("decode T=64 packed", "decode", beam_bf16_packed, oracle_weights=beam_bf16_weights)
+
+
+@pytest.fixture(scope="module")
+def beam_bf16_packed(beam_bf16_weights):
     pw = packed_copy(beam_bf16_weights)
     torch.cuda.synchronize()
-    try:
-        _full_shape("decode T=64 packed", "decode", pw, oracle_weights=beam_bf16_weights)
-    finally:
-        del pw
-        torch.cuda.empty_cache()
+    yield pw
+    del pw
+    torch.cuda.empty_cache()
 
 
-def test_beam_prefill_full_shape(beam_bf16_weights):
+def _pick(packed, w, pw):
+    return (pw, w) if packed else (w, None)
+
+
+@pytest.mark.parametrize("packed", LAYOUTS)
+def test_beam_prefill_full_shape(beam_bf16_weights, beam_bf16_packed, packed):
     def balanced(rep, cnt, out):
         assert rep["max_over_mean"] <= 1.05
-    _full_shape("prefill T=4096", "prefill", beam_bf16_weights, balanced)
+    w, ow = _pick(packed, beam_bf16_weights, beam_bf16_packed)
+    _full_shape("prefill T=4096" + (" packed" if packed else ""), "prefill", w, balanced, ow)
 
 
-def test_beam_skewed_full_shape(beam_bf16_weights):
+@pytest.mark.parametrize("packed", LAYOUTS)
+def test_beam_skewed_full_shape(beam_bf16_weights, beam_bf16_packed, packed):
     def skewed(rep, cnt, out):
         assert cnt[:8].min() >= 4 * cnt.mean()   # the +0.5 bias makes experts 0-7 hot
         assert int(cnt.sum()) == 8 * 16384
-    _full_shape("skewed T=16384", "skewed", beam_bf16_weights, skewed)
+    w, ow = _pick(packed, beam_bf16_weights, beam_bf16_packed)
+    _full_shape("skewed T=16384" + (" packed" if packed else ""), "skewed", w, skewed, ow)
 
 
 def test_beam_fp8_full_shape():
     dev = _dev()
     cfg = workloads.workload("fp8")
     w8 = workloads.make_expert_weights(cfg, 0, dev)
+    pw8 = packed_copy(w8)
     torch.cuda.synchronize()
     try:
         _full_shape("fp8 T=8192", "fp8", w8)
+        _full_shape("fp8 T=8192 packed", "fp8", pw8, oracle_weights=w8)
     finally:
-        del w8
+        del w8, pw8
         torch.cuda.empty_cache()

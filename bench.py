@@ -30,7 +30,9 @@ Printed fields beyond the usual ones:
 Other modes: --workload tiny|decode|prefill|skewed|fp8 picks the timed
 workload; --calibrate-copy runs one plain device copy of 1 GiB before the
 timed region (for counter calibration); --summarize DIR prints a summary of
-a rocprofv3 output directory (kernel stats or counter collection).
+a rocprofv3 output directory (kernel stats or counter collection);
+--traffic FETCH_DIR WRITE_DIR --workload W writes the counter summary that
+the traffic field reads.
 """
 
 import argparse
@@ -51,7 +53,21 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 KERNEL_SOURCES = ["group_limited_routing_amd/csrc/expert_gemm.hip",
                   "group_limited_routing_amd/csrc/common.h"]
-DOMINANT_KERNEL = "gemm_stream_kernel / gemm_tiled_kernel (gate/up pass)"
+COPY_CAL_KIB = 1 << 20          # the calibration copy moves 1 GiB each way
+
+
+def gateup_kernel(cfg):
+    """Name of the kernel the library launches for the gate/up pass of this
+    workload with packed weights (same rules as its launcher)."""
+    pairs = cfg["T"] * cfg["top_k"]
+    xt = "float" if cfg["x_dtype"] == "f32" else "unsigned short"
+    fp8 = cfg["w_dtype"] == "fp8"
+    if pairs <= 16 * cfg["n_experts"]:
+        return f"gemm_stream_kernel<0, {'unsigned char' if fp8 else xt}, {str(fp8).lower()}, true, ...>"
+    bm = 256 if pairs >= 192 * cfg["n_experts"] else 128
+    if not fp8 and xt == "unsigned short":
+        return f"gemm_dma_kernel<0, {bm}>"
+    return f"gemm_wide_kernel<0, {'unsigned char' if fp8 else xt}, {str(fp8).lower()}, {bm}>"
 
 
 def kernel_source_sha():
@@ -252,6 +268,59 @@ def summarize(d):
             print(f"{n:>10} {tot / n:>20.1f}  {cname}  {kname}")
 
 
+def _counter_rows(d):
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir, workload):
+    """Turn one FETCH_SIZE pass and one WRITE_SIZE pass (rocprofv3 --pmc, KiB per
+    dispatch) over `bench.py --workload W --no-prefill --calibrate-copy` into
+    HBM bytes per gate/up launch. Each counter is scaled by what it reads for
+    the 1 GiB device copy made before the timed region (the largest copyBuffer
+    dispatch of the run)."""
+    import re
+    pat = re.compile(r"beam::gemm_\w+<0,")
+    out = {}
+    for name, d in (("fetch", fetch_dir), ("write", write_dir)):
+        rows = _counter_rows(d)
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        gu = [r for r in rows if pat.search(r["Kernel_Name"])]
+        kernels = sorted({r["Kernel_Name"] for r in gu})
+        if len(kernels) != 1:
+            raise SystemExit(f"expected one gate/up kernel in {d}, found {kernels}")
+        out[name] = {"copy_kib": copy, "factor": COPY_CAL_KIB / copy,
+                     "kib": sum(float(r["Counter_Value"]) for r in gu) / len(gu),
+                     "n": len(gu), "kernel": kernels[0]}
+    f, w = out["fetch"], out["write"]
+    hbm = (f["kib"] * f["factor"] + w["kib"] * w["factor"]) * 1024
+    cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <dir> -o run --output-format csv "
+           f"-- python3 /root/repo/bench.py --workload {workload} --steps 3 --warmup 1 --no-prefill "
+           "--no-cpu-baseline --calibrate-copy")
+    path = os.path.join(ROOT, "profiles", f"gateup_{workload}_counters.txt")
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic of the gate/up grouped GEMM, workload {workload}, one MI355X\n")
+        fh.write("# commands (one counter per pass):\n")
+        fh.write("#   " + cmd.format(c="FETCH_SIZE") + "\n")
+        fh.write("#   " + cmd.format(c="WRITE_SIZE") + "\n")
+        fh.write(f"#   python3 bench.py --traffic <fetch dir> <write dir> --workload {workload}\n")
+        fh.write("# calibration: a 1 GiB device copy reads and writes 1048576 KiB\n")
+        fh.write(f"kernel = {f['kernel']}\n")
+        fh.write(f"dispatches = {f['n']}\n")
+        fh.write(f"fetch_kib_per_dispatch = {f['kib']:.1f}\n")
+        fh.write(f"write_kib_per_dispatch = {w['kib']:.1f}\n")
+        fh.write(f"copy_fetch_kib = {f['copy_kib']:.1f}\n")
+        fh.write(f"copy_write_kib = {w['copy_kib']:.1f}\n")
+        fh.write(f"fetch_factor = {f['factor']:.4f}\n")
+        fh.write(f"write_factor = {w['factor']:.4f}\n")
+        fh.write(f"hbm_bytes_per_launch = {hbm:.0f}\n")
+        fh.write(f"kernel_source_sha = {kernel_source_sha()}\n")
+    print(open(path).read())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,13 +330,17 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
 
     if args.summarize:
         summarize(args.summarize)
+        return 0
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.workload)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -311,7 +384,7 @@ def main():
                    "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "top_k": cfg["top_k"],
                    "active_experts": bench.active, "max_over_mean_load": round(bench.max_over_mean, 4),
                    "parallelism": "single GPU"},
-        "roofline": dict(rl, kernel=DOMINANT_KERNEL, launch_ms=round(res["gateup_ms"], 4),
+        "roofline": dict(rl, kernel=gateup_kernel(cfg), launch_ms=round(res["gateup_ms"], 4),
                          algorithmic_bytes=gb, algorithmic_flops=gf),
         "layer": {"pct_hbm": round(lb / step_s / 1e9 / HBM_PEAK_GBS, 4),
                   "pct_mfma": round(lf / step_s / 1e12 / MFMA_PEAK_TFLOPS[wdt], 4),
@@ -329,7 +402,8 @@ def main():
             "ms_per_step": round(pres["ms_per_step"], 4), "steps": args.prefill_steps,
             "max_over_mean_load": round(pb.max_over_mean, 4),
             "roofline": dict(roofline(pgb, pgf, pres["gateup_ms"] / 1e3, "bf16", stored_traffic("prefill")),
-                             launch_ms=round(pres["gateup_ms"], 4)),
+                             kernel=gateup_kernel(pcfg), launch_ms=round(pres["gateup_ms"], 4),
+                             algorithmic_bytes=pgb, algorithmic_flops=pgf),
             "layer": {"pct_hbm": round(plb / ps / 1e9 / HBM_PEAK_GBS, 4),
                       "pct_mfma": round(plf / ps / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
                       "stages_ms": pres["stages_ms"]},

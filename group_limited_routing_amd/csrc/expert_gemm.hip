@@ -733,7 +733,11 @@ void gemm_wide_kernel(GemmArgs p) {
 // computed. Waits are explicit: before stage kt is read, vmcnt leaves only
 // the DMAs of the later stages outstanding, and a raw barrier publishes every
 // wave's stage-kt DMAs. Each wave consumes its LDS reads (its MFMAs need
-// them) before the barrier that lets a stage buffer be refilled.
+// them) before the barrier that lets a stage buffer be refilled. A wave
+// whose rows are partly past the expert's last row runs a copy of the loop
+// that reads and multiplies only its first FM/4 or FM/2 fragments (none if
+// no row is live), so an expert slightly over a tile boundary costs little
+// matrix-core time in a 256-row tile.
 //
 // LDS per stage: A is BM rows x 64 bytes, row r's chunk g (16 bytes) stored at
 // position g ^ ((r >> 1) & 3) so the 16 rows of a fragment read hit distinct
@@ -815,8 +819,6 @@ void gemm_dma_kernel(GemmArgs p) {
     const int rbl = (MODE == 0) ? ((f < 2) ? wn * 2 + f : 8 + wn * 2 + (f - 2)) : wn * 4 + f;
     boff[f] = A_BYTES + rbl * 1024 + lane * 16;
   }
-  const bool live = wm * (BM / 2) < ti.rows;
-
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -824,32 +826,48 @@ void gemm_dma_kernel(GemmArgs p) {
     for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / 32;  // >= 4 since K is a multiple of 128
+  // The k loop for a wave whose live rows fit in its first NF fragments
+  // (NF = 0: a wave with no live rows only takes part in the loads and
+  // barriers). Every variant issues the same DMAs and barriers.
+  auto kloop = [&](auto nf_c) {
+    constexpr int NF = decltype(nf_c)::value;
 #pragma unroll
-  for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt done for this wave: at most the later issued stages outstanding
-    if (kt + NS - 2 < nk)
-      wait_vmcnt<(NS - 2) * PER_STAGE>();
-    else
-      wait_vmcnt<0>();
-    barrier_only();  // ... and for every wave; all reads of kt - 1 retired
-    asm volatile("" ::: "memory");
-    if (kt + NS - 1 < nk) issue(kt + NS - 1);  // refills the slot read at kt - 1
-    if (live) {
-      const uint8_t* st = smem + (kt % NS) * STAGE;
-      u32x4 af[FM], bfr[FN];
+    for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0);
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt done for this wave: at most the later issued stages outstanding
+      if (kt + NS - 2 < nk)
+        wait_vmcnt<(NS - 2) * PER_STAGE>();
+      else
+        wait_vmcnt<0>();
+      barrier_only();  // ... and for every wave; all reads of kt - 1 retired
+      asm volatile("" ::: "memory");
+      if (kt + NS - 1 < nk) issue(kt + NS - 1);  // refills the slot read at kt - 1
+      if constexpr (NF > 0) {
+        const uint8_t* st = smem + (kt % NS) * STAGE;
+        u32x4 af[NF], bfr[FN];
 #pragma unroll
-      for (int f = 0; f < FN; ++f) bfr[f] = ld16(st + boff[f]);
+        for (int f = 0; f < FN; ++f) bfr[f] = ld16(st + boff[f]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = ld16(st + aoff[i]);
+        for (int i = 0; i < NF; ++i) af[i] = ld16(st + aoff[i]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < NF; ++i)
 #pragma unroll
-        for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_op(bfr[jn], af[i], acc[i][jn]);
+          for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_op(bfr[jn], af[i], acc[i][jn]);
+      }
+      wait_lgkmcnt0();
+      asm volatile("" ::: "memory");
     }
-    wait_lgkmcnt0();
-    asm volatile("" ::: "memory");
-  }
+  };
+  // fragments of this wave that hold live rows
+  const int need = min(FM, max(0, (ti.rows - wm * (BM / 2) + 15) >> 4));
+  if (need == 0)
+    kloop(std::integral_constant<int, 0>{});
+  else if (need <= FM / 4)
+    kloop(std::integral_constant<int, FM / 4>{});
+  else if (need <= FM / 2)
+    kloop(std::integral_constant<int, FM / 2>{});
+  else
+    kloop(std::integral_constant<int, FM>{});
 
   transposed_epilogue<MODE, false, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
 }
@@ -890,8 +908,14 @@ static void launch_tiled(const Shape& s, const GemmArgs& g, hipStream_t st) {
 }
 
 int wide_bm(const Shape& s) {
-  // 256-row tiles once experts average 192 rows or more
-  return (long long)s.T * s.top_k >= 192LL * s.E ? 256 : 128;
+  // An expert whose rows span two M-tiles has its weights read once per tile
+  // (the second read hits L2 only when both tiles run in step). The DMA
+  // variant skips the matrix-core work of fragments without live rows, so it
+  // takes 256-row tiles once experts average 96 rows; the register-staged
+  // variant computes whole tiles and switches at 192.
+  const long long pairs = (long long)s.T * s.top_k;
+  const bool dma = !s.w_fp8 && !s.x_f32;
+  return pairs >= (dma ? 96LL : 192LL) * s.E ? 256 : 128;
 }
 
 template <int MODE, typename AT, bool FP8, int BM>

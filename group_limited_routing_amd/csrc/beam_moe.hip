@@ -54,6 +54,14 @@ Layout make_layout(const Shape& s) {
     L.h = take(P * I * 2);   // bf16 SwiGLU output
   }
   L.y = take(P * H * 2);     // bf16 expert outputs, scaled by rsf * w
+  if (!s.x_f32) {
+    L.router_ks = router_ksplit(s.T, s.H);
+    L.wsplit = take(3 * E * H * 2);
+    L.zpart = take((size_t)L.router_ks * T * E * 4);
+  } else {
+    L.router_ks = 0;
+    L.wsplit = L.zpart = 0;
+  }
   L.total = off;
   return L;
 }
@@ -165,6 +173,8 @@ beam_status staged(int stage, hipStream_t st, F&& launch) {
 // arrays when `permute` is set; `BM` is the M-tile height of the expert GEMMs.
 struct Buffers {
   float* z;
+  float* zpart;
+  uint16_t* wsplit;
   int32_t* idx;
   float* w;
   int32_t *chist, *cbase, *counts, *offsets, *meta, *tile_e, *tile_r, *e_tstart, *e_ntiles, *stok,
@@ -176,6 +186,8 @@ Buffers carve(const Layout& L, void* ws) {
   uint8_t* b = (uint8_t*)ws;
   Buffers B;
   B.z = (float*)(b + L.z);
+  B.zpart = (float*)(b + L.zpart);
+  B.wsplit = (uint16_t*)(b + L.wsplit);
   B.idx = (int32_t*)(b + L.idx);
   B.w = (float*)(b + L.w);
   B.chist = (int32_t*)(b + L.chist);
@@ -191,6 +203,27 @@ Buffers carve(const Layout& L, void* ws) {
   B.sw = (float*)(b + L.sw);
   B.inv = (int32_t*)(b + L.inv);
   return B;
+}
+
+// Router logits and selection. bf16 tokens: split weights, partial logits,
+// summed by the selection (which stores them when logits are requested).
+// fp32 tokens: fp32 MFMA logits straight into z.
+beam_status route_tokens(const Shape& s, const Layout& L, const Buffers& B, const void* x,
+                         const float* router_w, const float* bias, float* logits_out,
+                         int32_t* idx, float* w, hipStream_t st) {
+  const int T = s.T;
+  if (L.router_ks > 0) {
+    STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_x3((const uint16_t*)x, router_w, B.wsplit, B.zpart,
+                                                     T, s.H, L.router_ks, st));
+    STAGE(BEAM_STAGE_SELECT, launch_select(B.zpart, L.router_ks, (size_t)T * s.E, logits_out, bias, T,
+                                           s.n_group, s.topk_group, s.top_k, idx, w, st));
+  } else {
+    float* z = logits_out ? logits_out : B.z;
+    STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
+    STAGE(BEAM_STAGE_SELECT, launch_select(z, 1, 0, nullptr, bias, T, s.n_group, s.topk_group,
+                                           s.top_k, idx, w, st));
+  }
+  return BEAM_OK;
 }
 
 }  // namespace
@@ -236,9 +269,9 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
 
   hipStream_t st = (hipStream_t)stream;
   Buffers B = carve(L, workspace);
-  float* z = router_logits ? router_logits : B.z;
-  STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
-  STAGE(BEAM_STAGE_SELECT, launch_select(z, expert_bias, T, s.n_group, s.topk_group, s.top_k, topk_idx, topk_w, st));
+  const beam_status rs = route_tokens(s, L, B, x, router_w, expert_bias, router_logits, topk_idx,
+                                      topk_w, st);
+  if (rs != BEAM_OK) return rs;
   if (expert_counts) {
     STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(topk_idx, T, s.top_k, B.chist, st));
     STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, kTiledBM, B.cbase, B.counts, B.offsets,
@@ -276,14 +309,14 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
   hipStream_t st = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   Buffers B = carve(L, workspace);
-  float* z = router_logits_out ? router_logits_out : B.z;
   int32_t* idx = topk_idx_out ? topk_idx_out : B.idx;
   float* w = topk_w_out ? topk_w_out : B.w;
   const int k = s.top_k;
   const int BM = use_stream_gemm(s) ? kStreamBM : (s.w_packed ? wide_bm(s) : kTiledBM);
 
-  STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
-  STAGE(BEAM_STAGE_SELECT, launch_select(z, expert_bias, T, s.n_group, s.topk_group, k, idx, w, st));
+  const beam_status rs = route_tokens(s, L, B, x, router_w, expert_bias, router_logits_out, idx, w,
+                                      st);
+  if (rs != BEAM_OK) return rs;
   STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(idx, T, k, B.chist, st));
   STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts, B.offsets, B.meta,
                                B.tile_e, B.tile_r, B.e_tstart, B.e_ntiles, expert_counts_out, st));

@@ -23,7 +23,9 @@ struct Shape {
 struct Layout {
   size_t z, idx, w, chist, cbase, counts, offsets, meta, tile_e, tile_r, e_tstart, e_ntiles;
   size_t stok, sw, inv, xq, xs, hamax, h, hq, hs, y, total;
+  size_t wsplit, zpart;  // bf16 tokens: split router weights, partial logits
   int nchunks, max_mtiles;
+  int router_ks;         // K ranges of the partial logits (0: fp32 router)
 };
 
 Layout make_layout(const Shape& s);
@@ -34,8 +36,14 @@ int mtile_bound(const Shape& s, int BM);
 
 hipError_t launch_router_logits(const void* x, int x_f32, const float* W, float* z, int T, int H,
                                 hipStream_t st);
-hipError_t launch_select(const float* z, const float* bias, int T, int n_group, int topk_group,
-                         int top_k, int32_t* idx, float* w, hipStream_t st);
+// bf16 tokens: router weights split into three bf16 parts, partial logits
+// over router_ksplit(T, H) ranges of the hidden dimension.
+int router_ksplit(int T, int H);
+hipError_t launch_router_x3(const uint16_t* x, const float* W, uint16_t* wsplit, float* zp, int T,
+                            int H, int ks, hipStream_t st);
+hipError_t launch_select(const float* z, int nparts, size_t pstride, float* zout, const float* bias,
+                         int T, int n_group, int topk_group, int top_k, int32_t* idx, float* w,
+                         hipStream_t st);
 hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int32_t* chist, hipStream_t st);
 hipError_t launch_perm_scan(const int32_t* chist, int nchunks, int BM, int32_t* cbase,
                             int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,

@@ -11,6 +11,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace beam {
 
 // z[t, e] = sum_h x[t, h] * W[e, h] in fp32.
@@ -101,6 +103,163 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   }
 }
 
+// ------------------------------------------------------------------ bf16 x 3
+// With bf16 tokens the fp32 logits can run on the bf16 matrix cores without
+// changing the arithmetic: every fp32 weight is the exact sum of three bf16
+// values (hi = w with the low 16 bits cleared, mid = the same for w - hi,
+// lo = w - hi - mid, which has at most 8 significant bits), and a bf16 x bf16
+// product is exact in fp32. So x . w = x . hi + x . mid + x . lo with exact
+// products and fp32 accumulation, like an fp32 dot product, at the bf16 rate.
+
+// W [256, H] fp32 -> three bf16 matrices (hi, mid, lo), each [256, H] in the
+// packed MFMA fragment order: the 16 rows x 32 columns of one operand are one
+// 1 KB block, lane l = (row % 16) + 16 * (column % 32 / 8) holding 8
+// consecutive columns. One thread per 8 consecutive columns of a row.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ W, int H,
+                                                           uint16_t* __restrict__ ws) {
+  const int chunks = H / 8;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= kExperts * chunks) return;
+  const int r = q / chunks, c0 = (q - r * chunks) * 8;
+  const u32x4 v0 = ld16(W + (size_t)r * H + c0), v1 = ld16(W + (size_t)r * H + c0 + 4);
+  uint32_t part[3][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t u = (i < 4) ? v0[i] : v1[i - 4];
+    const uint32_t hi = u & 0xffff0000u;
+    const float r1 = __uint_as_float(u) - __uint_as_float(hi);  // exact
+    const uint32_t mid = __float_as_uint(r1) & 0xffff0000u;
+    const float lo = r1 - __uint_as_float(mid);                  // exact, <= 8 bits
+    const uint32_t b[3] = {hi >> 16, mid >> 16, __float_as_uint(lo) >> 16};
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp) {
+      if (i & 1)
+        part[sp][i >> 1] |= b[sp] << 16;
+      else
+        part[sp][i >> 1] = b[sp];
+    }
+  }
+  const size_t off = ((size_t)(r >> 4) * (H / 32) + (c0 >> 5)) * 512 +
+                     (size_t)((r & 15) + 16 * ((c0 & 31) >> 3)) * 8;
+#pragma unroll
+  for (int sp = 0; sp < 3; ++sp)
+    st16(ws + (size_t)sp * kExperts * H + off,
+         u32x4{part[sp][0], part[sp][1], part[sp][2], part[sp][3]});
+}
+
+// Partial logits zp[kz, t, e] = sum over the kz-th K range of x[t, h] * W[e, h]
+// (gridDim.z ranges), on 16x16x32 bf16 MFMAs with the split weights.
+// Workgroup: 256 tokens x 128 experts, 8 waves as 4 (tokens) x 2 (experts),
+// each 64 x 64. Operands go global -> LDS by DMA through a ring of 3 stages of
+// 32 k: x rows (64 bytes per row, 16-byte chunk g of row r stored at position
+// g ^ ((r >> 1) & 3)) and 24 weight blocks (3 parts x 8 row blocks of 1 KB).
+// The weight fragment is the MFMA's first operand, so a lane ends with 4
+// consecutive experts of one token, stored as one 16-byte write.
+constexpr int kRxBM = 256, kRxBN = 128, kRxNS = 3;
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void router_x3_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ ws,
+                      float* __restrict__ zp, int T, int H) {
+  constexpr int NS = kRxNS, A_BYTES = kRxBM * 64, B_BYTES = 24 * 1024, STAGE = A_BYTES + B_BYTES;
+  constexpr int PER_STAGE = 5;  // DMAs per wave per stage: 2 x rows + 3 weight blocks
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1, r = lane & 15, g = lane >> 4;
+  const int tok0 = blockIdx.x * kRxBM, e0 = blockIdx.y * kRxBN;
+  const int nk = (H / 32) / gridDim.z, kt0 = blockIdx.z * nk;
+
+  const uint16_t* asrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = (wave * 2 + i) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    asrc[i] = x + (size_t)min(tok0 + row, T - 1) * H + (size_t)kt0 * 32 + chunk * 8;
+  }
+  const uint16_t* bsrc[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int j = wave * 3 + i, sp = j >> 3, rb = j & 7;
+    bsrc[i] = ws + (size_t)sp * kExperts * H +
+              ((size_t)((e0 >> 4) + rb) * (H / 32) + kt0) * 512 + lane * 8;
+  }
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(asrc[i] + (size_t)kt * 32, st + (wave * 2 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) dma16(bsrc[i] + (size_t)kt * 512, st + A_BYTES + (wave * 3 + i) * 1024);
+  };
+
+  int aoff[4], boff[3][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int row = wm * 64 + f * 16 + r;
+    aoff[f] = row * 64 + ((g ^ ((row >> 1) & 3)) << 4);
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp) boff[sp][f] = A_BYTES + (sp * 8 + wn * 4 + f) * 1024 + lane * 16;
+  }
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The k loop; a wave whose 64 tokens are all past T only loads and syncs.
+  auto kloop = [&](auto live_c) {
+    constexpr bool LIVE = decltype(live_c)::value;
+#pragma unroll
+    for (int s0 = 0; s0 < NS - 1; ++s0)
+      if (s0 < nk) issue(s0);
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + NS - 2 < nk)
+        wait_vmcnt<(NS - 2) * PER_STAGE>();
+      else
+        wait_vmcnt<0>();
+      barrier_only();
+      asm volatile("" ::: "memory");
+      if (kt + NS - 1 < nk) issue(kt + NS - 1);
+      if constexpr (LIVE) {
+        const uint8_t* st = smem + (kt % NS) * STAGE;
+        u32x4 af[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) af[f] = ld16(st + aoff[f]);
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) {
+          u32x4 bfr[4];
+#pragma unroll
+          for (int f = 0; f < 4; ++f) bfr[f] = ld16(st + boff[sp][f]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i][j] = mfma_bf16(as_bf16x8(bfr[j]), as_bf16x8(af[i]), acc[i][j]);
+        }
+      }
+      wait_lgkmcnt0();
+      asm volatile("" ::: "memory");
+    }
+  };
+  if (tok0 + wm * 64 < T)
+    kloop(std::integral_constant<bool, true>{});
+  else
+    kloop(std::integral_constant<bool, false>{});
+
+  float* zo = zp + (size_t)blockIdx.z * T * kExperts;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = tok0 + wm * 64 + i * 16 + r;
+    if (t < T) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        st16(zo + (size_t)t * kExperts + e0 + wn * 64 + j * 16 + 4 * g,
+             u32x4{__float_as_uint(acc[i][j][0]), __float_as_uint(acc[i][j][1]),
+                   __float_as_uint(acc[i][j][2]), __float_as_uint(acc[i][j][3])});
+    }
+  }
+}
+
 // Best (key, index) of two candidates: larger key, equal keys to the lower
 // index; idx < 0 marks "no candidate".
 __device__ __forceinline__ void take_better(float& k, int& i, float ok, int oi) {
@@ -111,7 +270,10 @@ __device__ __forceinline__ void take_better(float& k, int& i, float ok, int oi) 
 
 // One wave per token. Lane l holds experts 4l..4l+3. A group of
 // 256/n_group experts spans lpg = 64/n_group lanes.
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ z,
+// The logits are the sum of `nparts` partial arrays (stride pstride floats),
+// added in order; with zout set the sum is also stored there.
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ z, int nparts,
+                                                     size_t pstride, float* __restrict__ zout,
                                                      const float* __restrict__ bias, int T,
                                                      int n_group, int topk_group, int top_k,
                                                      int32_t* __restrict__ idx,
@@ -120,7 +282,14 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ z
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
 
-  const u32x4 zv = ld16(z + (size_t)t * kExperts + 4 * lane);
+  const size_t zo = (size_t)t * kExperts + 4 * lane;
+  u32x4 zv = ld16(z + zo);
+  for (int p = 1; p < nparts; ++p) {
+    const u32x4 o = ld16(z + p * pstride + zo);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zv[i] = __float_as_uint(__uint_as_float(zv[i]) + __uint_as_float(o[i]));
+  }
+  if (zout) st16(zout + zo, zv);
   const u32x4 bv = ld16(bias + 4 * lane);
   float s[4], key[4];
 #pragma unroll
@@ -209,9 +378,29 @@ hipError_t launch_router_logits(const void* x, int x_f32, const float* W, float*
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* z, const float* bias, int T, int n_group, int topk_group,
-                         int top_k, int32_t* idx, float* w, hipStream_t st) {
-  select_kernel<<<(T + 3) / 4, 256, 0, st>>>(z, bias, T, n_group, topk_group, top_k, idx, w);
+int router_ksplit(int T, int H) {
+  // Enough workgroups for the 256 CUs (about 512): split the reduction when
+  // there are few 256-token tiles, into a power of two that divides H / 32.
+  const int tiles = 2 * ((T + kRxBM - 1) / kRxBM);
+  const int nk = H / 32;
+  int ks = 1;
+  while (ks < 16 && tiles * ks < 512 && nk % (2 * ks) == 0) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_router_x3(const uint16_t* x, const float* W, uint16_t* wsplit, float* zp, int T,
+                            int H, int ks, hipStream_t st) {
+  router_split_kernel<<<(kExperts * (H / 8) + 255) / 256, 256, 0, st>>>(W, H, wsplit);
+  dim3 grid((T + kRxBM - 1) / kRxBM, kExperts / kRxBN, ks);
+  router_x3_kernel<<<grid, 512, 0, st>>>(x, wsplit, zp, T, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float* z, int nparts, size_t pstride, float* zout, const float* bias,
+                         int T, int n_group, int topk_group, int top_k, int32_t* idx, float* w,
+                         hipStream_t st) {
+  select_kernel<<<(T + 3) / 4, 256, 0, st>>>(z, nparts, pstride, zout, bias, T, n_group,
+                                             topk_group, top_k, idx, w);
   return hipGetLastError();
 }
 

@@ -64,11 +64,13 @@ def gateup_kernel(cfg):
     fp8 = cfg["w_dtype"] == "fp8"
     if pairs <= 16 * cfg["n_experts"]:
         return f"gemm_stream_kernel<0, {'unsigned char' if fp8 else xt}, {str(fp8).lower()}, true, ...>"
-    dma = not fp8 and xt == "unsigned short"
+    dma = fp8 or xt == "unsigned short"
     bm = 256 if pairs >= (96 if dma else 192) * cfg["n_experts"] else 128
+    if fp8:
+        return f"gemm_dma8_kernel<0, {bm}>"
     if dma:
         return f"gemm_dma_kernel<0, {bm}>"
-    return f"gemm_wide_kernel<0, {'unsigned char' if fp8 else xt}, {str(fp8).lower()}, {bm}>"
+    return f"gemm_wide_kernel<0, {xt}, false, {bm}>"
 
 
 def kernel_source_sha():

@@ -31,6 +31,7 @@
 #include "common.h"
 #include "internal.h"
 
+
 namespace beam {
 
 // Per-type constants. One MFMA consumes KSTEP values of k; a lane's operand
@@ -872,6 +873,156 @@ void gemm_dma_kernel(GemmArgs p) {
   transposed_epilogue<MODE, false, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
 }
 
+// ---------------------------------------------------------------- fp8 DMA variant
+// Prefill with packed E4M3 weights and E4M3 A (x or h codes, per-row scales
+// applied in the epilogue). Same tiles, wave grid and tile order as the bf16
+// DMA variant; one matrix-core step is 128 k (16x16x128 fp8), loaded as two
+// half-stages of 64 k: A is BM rows x 64 bytes (chunk g of row r at position
+// g ^ ((r >> 1) & 3)), B is the first or second KB of each of the 16 row
+// blocks' 2 KB fragment blocks (lanes 0-31 of a fragment hold k 0..63, lanes
+// 32-63 k 64..127). The ring has NS half-stage slots and is filled NS - 2
+// half-stages ahead, so the two halves being read are never refilled: the
+// slot refilled at half-stage i last held half-stage i - 2, read by the step
+// that ended before barrier i. Lanes 0-31 read their operands from the
+// step's first half, lanes 32-63 from its second.
+template <int MODE, int BM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_dma8_kernel(GemmArgs p) {
+  constexpr int A_BYTES = BM * 64, B_BYTES = 16 * 1024, STAGE = A_BYTES + B_BYTES;
+  constexpr int NS = (160 * 1024) / STAGE;     // 5 (BM 256) or 6 (BM 128) slots
+  constexpr int AHEAD = NS - 2;
+  constexpr int FM = BM / 32, FN = 4;
+  constexpr int COLS = (MODE == 0) ? 128 : 256;
+  constexpr int AI = BM / 128;                 // A DMA instructions per wave per half-stage
+  constexpr int PER_STAGE = AI + 2;
+  static_assert(AHEAD >= 2, "ring too small");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const int ntn = p.N / COLS;
+  const int n_tiles = p.meta[0] * ntn;
+  const int b = blockIdx.x;
+  if (b >= n_tiles) return;
+  const int xcd = b & 7, per = n_tiles >> 3, extra = n_tiles & 7;
+  const int j = xcd * per + min(xcd, extra) + (b >> 3);
+  const int e = p.tile_e[j / ntn];
+  const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
+  const int jj = j - ts * ntn;
+  const int mb = jj / (kGroupM * ntn), rem = jj - mb * kGroupM * ntn;
+  const int gm = min(kGroupM, nm - mb * kGroupM);
+  const int nt = rem / gm, mt = ts + mb * kGroupM + rem % gm;
+  TileInfo ti;
+  ti.e = e;
+  ti.row0 = p.tile_r[mt];
+  ti.rows = min(BM, p.offsets[e + 1] - ti.row0);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3, r = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N;
+  const int n0 = nt * COLS;
+
+  // A: instruction i of this wave fills tile rows 16 * (wave * AI + i) ..;
+  // lane l writes row l / 4, position l % 4 (chunk (l % 4) ^ ((row >> 1) & 3)).
+  const uint8_t* asrc[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = (wave * AI + i) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    const int ar = min(row, ti.rows - 1);
+    const uint8_t* base = (MODE == 0) ? (const uint8_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K
+                                      : (const uint8_t*)p.a + (size_t)(ti.row0 + ar) * K;
+    asrc[i] = base + chunk * 16;
+  }
+  // B: instruction i fills row block wave * 2 + i (MODE 0: 0..7 gate, 8..15 up).
+  const uint8_t* bsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rbk = wave * 2 + i;
+    const uint8_t* W = (const uint8_t*)((MODE == 0 && rbk >= 8) ? p.w1 : p.w0);
+    const int blk = (MODE == 0) ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
+    bsrc[i] = W + (size_t)ti.e * N * K + (size_t)blk * 16 * K + lane * 16;
+  }
+  auto issue = [&](int hs) {  // half-stage hs: k bytes [64 hs, 64 hs + 64)
+    uint8_t* st = smem + (hs % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) dma16(asrc[i] + (size_t)hs * 64, st + (wave * AI + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma16(bsrc[i] + (size_t)(hs >> 1) * 2048 + (hs & 1) * 1024, st + A_BYTES + (wave * 2 + i) * 1024);
+  };
+
+  // Operand offsets inside a slot; this lane's half of the step is lane / 32.
+  const int half = lane >> 5, c0 = 2 * (g & 1);
+  int aoff[FM], boff[FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f) {
+    const int row = wm * (BM / 2) + f * 16 + r;
+    aoff[f] = row * 64 + ((c0 ^ ((row >> 1) & 3)) << 4);
+  }
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const int rbl = (MODE == 0) ? ((f < 2) ? wn * 2 + f : 8 + wn * 2 + (f - 2)) : wn * 4 + f;
+    boff[f] = A_BYTES + rbl * 1024 + (lane & 31) * 32;
+  }
+  // the second chunk of a row's 32 bytes sits at position (c0 + 1) ^ swizzle,
+  // which is the first position with its lowest bit flipped
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nh = K / 64;  // even, >= 2
+  auto kloop = [&](auto nf_c) {
+    constexpr int NF = decltype(nf_c)::value;
+#pragma unroll
+    for (int s0 = 0; s0 < AHEAD; ++s0)
+      if (s0 < nh) issue(s0);
+    for (int hs = 0; hs < nh; ++hs) {
+      // half-stage hs done for this wave: only later half-stages outstanding
+      if (hs + AHEAD - 1 < nh)
+        wait_vmcnt<(AHEAD - 1) * PER_STAGE>();
+      else
+        wait_vmcnt<0>();
+      barrier_only();
+      asm volatile("" ::: "memory");
+      if (hs + AHEAD < nh) issue(hs + AHEAD);
+      if constexpr (NF > 0) {
+        if (hs & 1) {
+          const uint8_t* st = smem + ((hs - 1 + half) % NS) * STAGE;
+          Op32 af[NF], bfr[FN];
+#pragma unroll
+          for (int f = 0; f < FN; ++f) {
+            bfr[f].lo = ld16(st + boff[f]);
+            bfr[f].hi = ld16(st + boff[f] + 16);
+          }
+#pragma unroll
+          for (int i = 0; i < NF; ++i) {
+            af[i].lo = ld16(st + aoff[i]);
+            af[i].hi = ld16(st + (aoff[i] ^ 16));
+          }
+#pragma unroll
+          for (int i = 0; i < NF; ++i)
+#pragma unroll
+            for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_op(bfr[jn], af[i], acc[i][jn]);
+        }
+      }
+      wait_lgkmcnt0();
+      asm volatile("" ::: "memory");
+    }
+  };
+  const int need = min(FM, max(0, (ti.rows - wm * (BM / 2) + 15) >> 4));
+  if (need == 0)
+    kloop(std::integral_constant<int, 0>{});
+  else if (need <= FM / 4)
+    kloop(std::integral_constant<int, FM / 4>{});
+  else if (need <= FM / 2)
+    kloop(std::integral_constant<int, FM / 2>{});
+  else
+    kloop(std::integral_constant<int, FM>{});
+
+  transposed_epilogue<MODE, true, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
+}
+
 // ---------------------------------------------------------------- launchers
 int mtile_bound(const Shape& s, int BM) {
   const long long pairs = (long long)s.T * s.top_k;
@@ -910,11 +1061,12 @@ static void launch_tiled(const Shape& s, const GemmArgs& g, hipStream_t st) {
 int wide_bm(const Shape& s) {
   // An expert whose rows span two M-tiles has its weights read once per tile
   // (the second read hits L2 only when both tiles run in step). The DMA
-  // variant skips the matrix-core work of fragments without live rows, so it
-  // takes 256-row tiles once experts average 96 rows; the register-staged
-  // variant computes whole tiles and switches at 192.
+  // variants (bf16 tokens, or fp8 weights) skip the matrix-core work of
+  // fragments without live rows, so they take 256-row tiles once experts
+  // average 96 rows; the register-staged variant (fp32 tokens, bf16 weights)
+  // computes whole tiles and switches at 192.
   const long long pairs = (long long)s.T * s.top_k;
-  const bool dma = !s.w_fp8 && !s.x_f32;
+  const bool dma = s.w_fp8 || !s.x_f32;
   return pairs >= (dma ? 96LL : 192LL) * s.E ? 256 : 128;
 }
 
@@ -924,7 +1076,9 @@ static void launch_wide_bm(const Shape& s, const GemmArgs& g, hipStream_t st) {
   // the 8 XCDs; blocks past the active count exit at once.
   long long n = (long long)mtile_bound(s, BM) * (g.N / (MODE == 0 ? 128 : 256));
   n = (n + 7) & ~7LL;
-  if constexpr (!FP8 && std::is_same<AT, uint16_t>::value)
+  if constexpr (FP8)
+    gemm_dma8_kernel<MODE, BM><<<(unsigned)n, 512, 0, st>>>(g);
+  else if constexpr (std::is_same<AT, uint16_t>::value)
     gemm_dma_kernel<MODE, BM><<<(unsigned)n, 512, 0, st>>>(g);
   else
     gemm_wide_kernel<MODE, AT, FP8, BM><<<(unsigned)n, 512, 0, st>>>(g);

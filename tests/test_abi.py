@@ -159,6 +159,6 @@ def test_library_links_every_kernel(L):
     syms = subprocess.run([nm, "-C", gl.LIB_PATH], capture_output=True, text=True, check=True).stdout
     for kernel in ["router_logits_kernel", "router_split_kernel", "router_x3_kernel", "select_kernel", "perm_hist_kernel", "perm_scan_kernel",
                    "perm_scatter_kernel", "gemm_stream_kernel", "gemm_tiled_kernel",
-                   "gemm_wide_kernel", "gemm_dma_kernel", "combine_kernel", "quant_x_kernel",
+                   "gemm_wide_kernel", "gemm_dma_kernel", "gemm_dma8_kernel", "combine_kernel", "quant_x_kernel",
                    "quant_h_kernel", "pack_kernel"]:
         assert f"__device_stub__{kernel}" in syms, kernel

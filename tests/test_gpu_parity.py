@@ -119,6 +119,25 @@ def test_fp8_tiled_variant(packed):
     _full_compare("fp8 tiled", cfg, 7, packed)
 
 
+def test_dma_variant_short_reduction():
+    # hidden 128: the gate/up reduction is 4 steps, shorter than the distance
+    # at which the next tile's first stages are loaded
+    cfg = _case(3000, 128, 256)
+    _full_compare("dma short K", cfg, 17, True)
+
+
+def test_fp8_dma_variant_128_rows():
+    cfg = _case(1000, 512, 256, w_dtype="fp8")   # ~31 rows per expert; down N = 512
+    _full_compare("fp8 dma 128", cfg, 15, True)
+
+
+def test_fp8_dma_variant_256_rows():
+    # ~100 rows per expert: 256-row tiles with partly live waves; the down
+    # pass has K = 128 (one fp8 step, shorter than the load-ahead distance)
+    cfg = _case(3200, 512, 128, w_dtype="fp8")
+    _full_compare("fp8 dma 256", cfg, 16, True)
+
+
 @pytest.mark.parametrize("dtype,S", [(torch.bfloat16, 32), (torch.float8_e4m3fn, 128)])
 def test_pack_layout_matches_definition(dtype, S):
     """The packed copy equals the documented layout, built here with a torch

@@ -22,16 +22,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits with the gfx950 conversion instruction: round to nearest
+// even, NaN stays NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Two fp32 values -> packed bf16 pair (lo in the low half), one instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) {
@@ -122,8 +124,10 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
   return 1.0f / (1.0f + expf(-z));
 }
 
+// silu(v) = v * sigmoid(v) in fp32 with the hardware base-2 exponential and
+// reciprocal (about one ulp each); the tails give v and -0 as they should.
 __device__ __forceinline__ float silu_f32(float v) {
-  return v / (1.0f + expf(-v));
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
 }
 
 }  // namespace beam

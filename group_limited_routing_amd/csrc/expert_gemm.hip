@@ -506,12 +506,27 @@ __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const Til
                                                     const f32x4 (&acc)[FM][FN], int row_base,
                                                     int n0, int wn, int r, int g) {
   const int N = p.N;
+  constexpr int NF = (MODE == 0) ? 2 : FN;  // output column blocks of this wave
+  // fp8: per-column weight scales of this lane's 4 columns, loaded once
+  f32x4 cs0[NF], cs1[NF];
+#pragma unroll
+  for (int fn = 0; fn < NF; ++fn) {
+    cs0[fn] = cs1[fn] = f32x4{1.f, 1.f, 1.f, 1.f};
+    if constexpr (FP8) {
+      const int n = n0 + (MODE == 0 ? (wn * 2 + fn) : (wn * 4 + fn)) * 16 + 4 * g;
+      const size_t c = (size_t)ti.e * N + n;
+      cs0[fn] = __builtin_bit_cast(f32x4, ld16(p.ws0 + c));
+      if constexpr (MODE == 0) cs1[fn] = __builtin_bit_cast(f32x4, ld16(p.ws1 + c));
+    }
+  }
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int row = row_base + fm * 16 + r;
     const bool valid = row < ti.rows;
     const size_t orow = (size_t)(ti.row0 + (valid ? row : 0)) * N;
-    if (MODE == 0) {
+    if constexpr (MODE == 0) {
+      // fp8: the token's activation scale
+      const float xs = (FP8 && valid) ? p.a_scale[p.stok[ti.row0 + row]] : 1.f;
       float rowmax = 0.f;
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn) {
@@ -519,7 +534,12 @@ __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const Til
         float h[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          h[i] = valid ? gateup_value<FP8>(p, ti, row, n + i, acc[fm][fn][i], acc[fm][fn + 2][i]) : 0.f;
+          float gv = acc[fm][fn][i], uv = acc[fm][fn + 2][i];
+          if constexpr (FP8) {
+            gv = gv * xs * cs0[fn][i];
+            uv = uv * xs * cs1[fn][i];
+          }
+          h[i] = valid ? silu_f32(gv) * uv : 0.f;
           rowmax = fmaxf(rowmax, fabsf(h[i]));
         }
         if (valid) {
@@ -539,12 +559,15 @@ __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const Til
       }
     } else {
       if (valid) {
+        // rsf * routing weight of the row (fp8: times the row's activation scale)
+        float rs = p.sw[ti.row0 + row];
+        if constexpr (FP8) rs = p.a_scale[ti.row0 + row] * rs;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           const int n = n0 + (wn * 4 + fn) * 16 + 4 * g;
           float y[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) y[i] = down_value<FP8>(p, ti, row, n + i, acc[fm][fn][i]);
+          for (int i = 0; i < 4; ++i) y[i] = FP8 ? acc[fm][fn][i] * cs0[fn][i] * rs : acc[fm][fn][i] * rs;
           *reinterpret_cast<u32x2*>((uint16_t*)p.out + orow + n) =
               u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
         }

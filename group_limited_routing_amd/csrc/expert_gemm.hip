@@ -499,21 +499,21 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
 // Epilogue of the transposed tiles (wide and DMA variants). acc[fm][fn]
 // holds, in lane (r, g), output row row_base + 16 fm + r and the 4 output
 // columns 16 c(fn) + 4 g .. + 3, where c(fn) is the fragment's column block:
-// gate/up: fn = 0, 1 gate and fn + 2 the matching up block, c = 2 wn + fn;
-// down: c = 4 wn + fn.
+// gate/up: fn < FN / 2 gate and fn + FN / 2 the matching up block,
+// c = (FN / 2) wn + fn; down: c = FN wn + fn.
 template <int MODE, bool FP8, int FM, int FN>
 __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const TileInfo& ti,
                                                     const f32x4 (&acc)[FM][FN], int row_base,
                                                     int n0, int wn, int r, int g) {
   const int N = p.N;
-  constexpr int NF = (MODE == 0) ? 2 : FN;  // output column blocks of this wave
+  constexpr int NF = (MODE == 0) ? FN / 2 : FN;  // output column blocks of this wave
   // fp8: per-column weight scales of this lane's 4 columns, loaded once
   f32x4 cs0[NF], cs1[NF];
 #pragma unroll
   for (int fn = 0; fn < NF; ++fn) {
     cs0[fn] = cs1[fn] = f32x4{1.f, 1.f, 1.f, 1.f};
     if constexpr (FP8) {
-      const int n = n0 + (MODE == 0 ? (wn * 2 + fn) : (wn * 4 + fn)) * 16 + 4 * g;
+      const int n = n0 + (wn * NF + fn) * 16 + 4 * g;
       const size_t c = (size_t)ti.e * N + n;
       cs0[fn] = __builtin_bit_cast(f32x4, ld16(p.ws0 + c));
       if constexpr (MODE == 0) cs1[fn] = __builtin_bit_cast(f32x4, ld16(p.ws1 + c));
@@ -529,12 +529,12 @@ __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const Til
       const float xs = (FP8 && valid) ? p.a_scale[p.stok[ti.row0 + row]] : 1.f;
       float rowmax = 0.f;
 #pragma unroll
-      for (int fn = 0; fn < 2; ++fn) {
-        const int n = n0 + (wn * 2 + fn) * 16 + 4 * g;
+      for (int fn = 0; fn < NF; ++fn) {
+        const int n = n0 + (wn * NF + fn) * 16 + 4 * g;
         float h[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float gv = acc[fm][fn][i], uv = acc[fm][fn + 2][i];
+          float gv = acc[fm][fn][i], uv = acc[fm][fn + NF][i];
           if constexpr (FP8) {
             gv = gv * xs * cs0[fn][i];
             uv = uv * xs * cs1[fn][i];
@@ -564,7 +564,7 @@ __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const Til
         if constexpr (FP8) rs = p.a_scale[ti.row0 + row] * rs;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-          const int n = n0 + (wn * 4 + fn) * 16 + 4 * g;
+          const int n = n0 + (wn * FN + fn) * 16 + 4 * g;
           float y[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) y[i] = FP8 ? acc[fm][fn][i] * cs0[fn][i] * rs : acc[fm][fn][i] * rs;

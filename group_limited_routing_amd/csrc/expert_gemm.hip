@@ -775,7 +775,7 @@ void gemm_dma_kernel(GemmArgs p) {
   constexpr int FM = BM / 32, FN = 4;
   constexpr int COLS = (MODE == 0) ? 128 : 256;
   constexpr int AI = BM / 128;                 // A DMA instructions per wave per stage
-  constexpr int PER_STAGE = AI + 2;            // DMA instructions per wave per stage
+  static_assert(AI == 1 || AI == 2, "row groups per wave");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
   const int ntn = p.N / COLS;
@@ -822,10 +822,14 @@ void gemm_dma_kernel(GemmArgs p) {
     const int blk = (MODE == 0) ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
     bsrc[i] = W + (size_t)ti.e * N * K + (size_t)blk * 16 * K + lane * 8;
   }
-  auto issue = [&](int kt) {  // DMA of k-step kt into ring slot kt % NS
+  // DMA of k-step kt into ring slot kt % NS: this wave's first AL row groups
+  // of A (the others lie past the expert's last row and are not loaded) and
+  // its two weight row blocks.
+  auto issue = [&](int kt, auto al_c) {
+    constexpr int AL = decltype(al_c)::value;
     uint8_t* st = smem + (kt % NS) * STAGE;
 #pragma unroll
-    for (int i = 0; i < AI; ++i)
+    for (int i = 0; i < AL; ++i)
       dma16(asrc[i] + (size_t)kt * 32, st + (wave * AI + i) * 1024);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -852,20 +856,22 @@ void gemm_dma_kernel(GemmArgs p) {
   const int nk = K / 32;  // >= 4 since K is a multiple of 128
   // The k loop for a wave whose live rows fit in its first NF fragments
   // (NF = 0: a wave with no live rows only takes part in the loads and
-  // barriers). Every variant issues the same DMAs and barriers.
-  auto kloop = [&](auto nf_c) {
+  // barriers) and that loads AL of its AI row groups of A. Every variant
+  // passes the same barriers; each waits for its own loads only.
+  auto kloop = [&](auto nf_c, auto al_c) {
     constexpr int NF = decltype(nf_c)::value;
+    constexpr int PER = decltype(al_c)::value + 2;  // this wave's DMAs per stage
 #pragma unroll
-    for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0);
+    for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0, al_c);
     for (int kt = 0; kt < nk; ++kt) {
       // stage kt done for this wave: at most the later issued stages outstanding
       if (kt + NS - 2 < nk)
-        wait_vmcnt<(NS - 2) * PER_STAGE>();
+        wait_vmcnt<(NS - 2) * PER>();
       else
         wait_vmcnt<0>();
       barrier_only();  // ... and for every wave; all reads of kt - 1 retired
       asm volatile("" ::: "memory");
-      if (kt + NS - 1 < nk) issue(kt + NS - 1);  // refills the slot read at kt - 1
+      if (kt + NS - 1 < nk) issue(kt + NS - 1, al_c);  // refills the slot read at kt - 1
       if constexpr (NF > 0) {
         const uint8_t* st = smem + (kt % NS) * STAGE;
         u32x4 af[NF], bfr[FN];
@@ -882,16 +888,26 @@ void gemm_dma_kernel(GemmArgs p) {
       asm volatile("" ::: "memory");
     }
   };
-  // fragments of this wave that hold live rows
+  // fragments of this wave that hold live rows, and its A row groups with
+  // live rows (row groups 16 (wave AI + i) ..)
   const int need = min(FM, max(0, (ti.rows - wm * (BM / 2) + 15) >> 4));
+  const int al = min(AI, max(0, (ti.rows - wave * AI * 16 + 15) >> 4));
+  auto run = [&](auto nf_c) {
+    if (al == 0)
+      kloop(nf_c, std::integral_constant<int, 0>{});
+    else if (al == 1)
+      kloop(nf_c, std::integral_constant<int, 1>{});
+    else
+      kloop(nf_c, std::integral_constant<int, AI>{});
+  };
   if (need == 0)
-    kloop(std::integral_constant<int, 0>{});
+    run(std::integral_constant<int, 0>{});
   else if (need <= FM / 4)
-    kloop(std::integral_constant<int, FM / 4>{});
+    run(std::integral_constant<int, FM / 4>{});
   else if (need <= FM / 2)
-    kloop(std::integral_constant<int, FM / 2>{});
+    run(std::integral_constant<int, FM / 2>{});
   else
-    kloop(std::integral_constant<int, FM>{});
+    run(std::integral_constant<int, FM>{});
 
   transposed_epilogue<MODE, false, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
 }

@@ -933,7 +933,6 @@ void gemm_dma8_kernel(GemmArgs p) {
   constexpr int FM = BM / 32, FN = 4;
   constexpr int COLS = (MODE == 0) ? 128 : 256;
   constexpr int AI = BM / 128;                 // A DMA instructions per wave per half-stage
-  constexpr int PER_STAGE = AI + 2;
   static_assert(AHEAD >= 2, "ring too small");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
@@ -980,10 +979,13 @@ void gemm_dma8_kernel(GemmArgs p) {
     const int blk = (MODE == 0) ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
     bsrc[i] = W + (size_t)ti.e * N * K + (size_t)blk * 16 * K + lane * 16;
   }
-  auto issue = [&](int hs) {  // half-stage hs: k bytes [64 hs, 64 hs + 64)
+  // half-stage hs (k bytes [64 hs, 64 hs + 64)): this wave's first AL row
+  // groups of A (the rest lie past the expert's last row) and two weight blocks
+  auto issue = [&](int hs, auto al_c) {
+    constexpr int AL = decltype(al_c)::value;
     uint8_t* st = smem + (hs % NS) * STAGE;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) dma16(asrc[i] + (size_t)hs * 64, st + (wave * AI + i) * 1024);
+    for (int i = 0; i < AL; ++i) dma16(asrc[i] + (size_t)hs * 64, st + (wave * AI + i) * 1024);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       dma16(bsrc[i] + (size_t)(hs >> 1) * 2048 + (hs & 1) * 1024, st + A_BYTES + (wave * 2 + i) * 1024);
@@ -1011,20 +1013,21 @@ void gemm_dma8_kernel(GemmArgs p) {
     for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nh = K / 64;  // even, >= 2
-  auto kloop = [&](auto nf_c) {
+  auto kloop = [&](auto nf_c, auto al_c) {
     constexpr int NF = decltype(nf_c)::value;
+    constexpr int PER = decltype(al_c)::value + 2;  // this wave's DMAs per half-stage
 #pragma unroll
     for (int s0 = 0; s0 < AHEAD; ++s0)
-      if (s0 < nh) issue(s0);
+      if (s0 < nh) issue(s0, al_c);
     for (int hs = 0; hs < nh; ++hs) {
       // half-stage hs done for this wave: only later half-stages outstanding
       if (hs + AHEAD - 1 < nh)
-        wait_vmcnt<(AHEAD - 1) * PER_STAGE>();
+        wait_vmcnt<(AHEAD - 1) * PER>();
       else
         wait_vmcnt<0>();
       barrier_only();
       asm volatile("" ::: "memory");
-      if (hs + AHEAD < nh) issue(hs + AHEAD);
+      if (hs + AHEAD < nh) issue(hs + AHEAD, al_c);
       if constexpr (NF > 0) {
         if (hs & 1) {
           const uint8_t* st = smem + ((hs - 1 + half) % NS) * STAGE;
@@ -1050,14 +1053,23 @@ void gemm_dma8_kernel(GemmArgs p) {
     }
   };
   const int need = min(FM, max(0, (ti.rows - wm * (BM / 2) + 15) >> 4));
+  const int al = min(AI, max(0, (ti.rows - wave * AI * 16 + 15) >> 4));
+  auto run = [&](auto nf_c) {
+    if (al == 0)
+      kloop(nf_c, std::integral_constant<int, 0>{});
+    else if (al == 1)
+      kloop(nf_c, std::integral_constant<int, 1>{});
+    else
+      kloop(nf_c, std::integral_constant<int, AI>{});
+  };
   if (need == 0)
-    kloop(std::integral_constant<int, 0>{});
+    run(std::integral_constant<int, 0>{});
   else if (need <= FM / 4)
-    kloop(std::integral_constant<int, FM / 4>{});
+    run(std::integral_constant<int, FM / 4>{});
   else if (need <= FM / 2)
-    kloop(std::integral_constant<int, FM / 2>{});
+    run(std::integral_constant<int, FM / 2>{});
   else
-    kloop(std::integral_constant<int, FM>{});
+    run(std::integral_constant<int, FM>{});
 
   transposed_epilogue<MODE, true, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
 }

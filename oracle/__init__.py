@@ -36,3 +36,4 @@ Parity status: every function here is pinned by the CPU tests
 from .routing import sigmoid, group_scores, select_from_keys, route  # noqa: F401
 from .experts import expert_ffn, forward, forward_tokens, dense_forward  # noqa: F401
 from . import e4m3  # noqa: F401
+from . import mxfp4  # noqa: F401

@@ -37,6 +37,7 @@ WORKLOADS = {
     "prefill": dict(T=4096, x_dtype="bf16", w_dtype="bf16", bias="balanced"),
     "skewed": dict(T=16384, x_dtype="bf16", w_dtype="bf16", bias="hot"),
     "fp8": dict(T=8192, x_dtype="bf16", w_dtype="fp8", bias="normal"),
+    "mxfp4": dict(T=64, x_dtype="bf16", w_dtype="mxfp4", bias="normal"),
 }
 
 DATA_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "data")
@@ -107,6 +108,34 @@ def make_small_inputs(cfg, seed=0):
     return x, router_w, bias
 
 
+# E2M1 magnitudes and the midpoints between neighbours (storage format of the
+# 4-bit checkpoint: OCP MXFP4, blocks of 32 along the reduction dimension).
+_E2M1_MID = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+
+
+def mxfp4_quantize(w):
+    """OCP MXFP4 of an fp32 [rows, K] tensor (K a multiple of 32), as stored
+    in the checkpoint: (codes [rows, K/2] uint8, element 2j in the low nibble;
+    scale codes [rows, K/32] uint8, E8M0). Block exponent floor(log2 amax) - 2;
+    elements rounded to the nearest E2M1 value, ties to the even code,
+    saturating at 6; an all-zero block takes scale code 0."""
+    rows, K = w.shape
+    b = w.reshape(rows, K // 32, 32)
+    amax = b.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)  # amax = m * 2^ex, m in [0.5, 1)
+    e = torch.where(amax > 0, ex.to(torch.int64) - 3, torch.full_like(ex, -127, dtype=torch.int64))
+    e = e.clamp(-127, 127)
+    scaled = b / torch.ldexp(torch.ones_like(amax), e.to(torch.float32))[..., None]
+    a = scaled.abs().clamp(max=6.0)
+    mid = torch.tensor(_E2M1_MID, dtype=torch.float32, device=w.device)
+    idx = torch.bucketize(a, mid)  # number of midpoints below a (a tie counts as below)
+    tie = (idx < len(_E2M1_MID)) & (a == mid[idx.clamp(max=len(_E2M1_MID) - 1)])
+    idx = torch.where(tie & (idx % 2 == 1), idx + 1, idx)  # ties to the even code
+    codes = (idx | torch.where(torch.signbit(scaled), 8, 0)).to(torch.uint8).reshape(rows, K)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    return packed.contiguous(), (e + 127).to(torch.uint8)
+
+
 def make_expert_weights(cfg, seed=0, device="cpu", experts=None):
     """Expert weights in storage format on ``device``.
 
@@ -115,10 +144,26 @@ def make_expert_weights(cfg, seed=0, device="cpu", experts=None):
     fp32 scales w_gate_scale [E, I], w_up_scale [E, I], w_down_scale [E, H];
     each row was quantised from its N(0, 0.02^2) draw with scale amax/448
     (checkpoint preparation, done with torch's own fp8 cast).
+    mxfp4: codes [E, I, H/2] / [E, H, I/2] uint8 (two E2M1 codes per byte)
+    plus E8M0 block scales w_*_scale [E, I, H/32] / [E, H, I/32] uint8
+    (``mxfp4_quantize`` of the same N(0, 0.02^2) draws).
     ``experts`` restricts generation to a list of expert indices (the other
     rows are left zero), for tests that only need a few experts.
     """
     E, H, I = cfg["n_experts"], cfg["hidden"], cfg["intermediate"]
+    if cfg["w_dtype"] == "mxfp4":
+        shapes = {"w_gate": (I, H), "w_up": (I, H), "w_down": (H, I)}
+        out = {}
+        for k, (R, C) in shapes.items():
+            out[k] = torch.zeros((E, R, C // 2), dtype=torch.uint8, device=device)
+            out[k + "_scale"] = torch.zeros((E, R, C // 32), dtype=torch.uint8, device=device)
+        ids = range(E) if experts is None else experts
+        for e in ids:
+            for k, s in shapes.items():
+                w = normal(s, 0.02, seed, k, e, device)
+                out[k][e], out[k + "_scale"][e] = mxfp4_quantize(w)
+                del w
+        return out
     fp8 = cfg["w_dtype"] == "fp8"
     store = torch.float8_e4m3fn if fp8 else torch.bfloat16
     shapes = {"w_gate": (I, H), "w_up": (I, H), "w_down": (H, I)}

@@ -82,7 +82,7 @@ def test_zero_block_and_nibble_order():
     assert sc[0, 0] == 0 and sc[0, 1] == 0 and sc[1, 0] == 0
     packed = mxfp4.pack_nibbles(codes)
     assert packed.shape == (2, 32)
-    assert packed[1, 16] == (codes[1, 33] << 4) and codes[1, 33] == 4  # 1.0 at scale 0.25
+    assert packed[1, 16] == (codes[1, 33] << 4) and codes[1, 33] == 6  # 1.0 = 4.0 (code 6) x 0.25
     assert np.array_equal(mxfp4.unpack_nibbles(packed), codes)
     deq = mxfp4.dequantize(packed, sc)
     assert deq[1, 33] == 1.0 and np.count_nonzero(deq) == 1

@@ -50,6 +50,8 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s at Beam shape (T=64 decode, T=4096 prefill) + % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
+# bytes per weight: MXFP4 is half a byte plus one scale byte per 32 weights
+WEIGHT_BYTES = {"bf16": 2, "fp8": 1, "mxfp4": 0.5 + 1 / 32}
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 KERNEL_SOURCES = ["group_limited_routing_amd/csrc/expert_gemm.hip",
                   "group_limited_routing_amd/csrc/common.h"]
@@ -62,6 +64,8 @@ def gateup_kernel(cfg):
     pairs = cfg["T"] * cfg["top_k"]
     xt = "float" if cfg["x_dtype"] == "f32" else "unsigned short"
     fp8 = cfg["w_dtype"] == "fp8"
+    if cfg["w_dtype"] == "mxfp4":
+        return "gemm_stream4_kernel<0, 8, 2>"
     if pairs <= 16 * cfg["n_experts"]:
         return f"gemm_stream_kernel<0, {'unsigned char' if fp8 else xt}, {str(fp8).lower()}, true, ...>"
     dma = fp8 or xt == "unsigned short"
@@ -82,7 +86,9 @@ def kernel_source_sha():
 
 
 def describe(cfg):
-    wdesc = "fp8 e4m3 weights, per-row scales" if cfg["w_dtype"] == "fp8" else "bf16 weights"
+    wdesc = {"fp8": "fp8 e4m3 weights, per-row scales",
+             "mxfp4": "MXFP4 weights (e2m1, e8m0 scale per 32), e4m3 activations"}.get(
+                 cfg["w_dtype"], "bf16 weights")
     return (f"{cfg['name']}: T={cfg['T']} tokens, hidden {cfg['hidden']}, {cfg['n_experts']} experts "
             f"x SwiGLU {cfg['intermediate']}, {wdesc}, x {cfg['x_dtype']}, group-limited top-{cfg['top_k']} "
             f"({cfg['n_group']} groups, keep {cfg['topk_group']}), scale {cfg['routed_scaling_factor']}")
@@ -91,13 +97,13 @@ def describe(cfg):
 def gateup_work(cfg, active):
     """Algorithmic bytes and flops of one gate/up launch."""
     T, H, I, k = cfg["T"], cfg["hidden"], cfg["intermediate"], cfg["top_k"]
-    wb = 1 if cfg["w_dtype"] == "fp8" else 2
+    wb = WEIGHT_BYTES[cfg["w_dtype"]]
     xb = 4 if cfg["x_dtype"] == "f32" else 2
-    if cfg["w_dtype"] == "fp8":
+    if cfg["w_dtype"] in ("fp8", "mxfp4"):
         x_read, h_write = T * H * 1, T * k * I * 4   # e4m3 x codes in, fp32 h out
     else:
         x_read, h_write = T * H * xb, T * k * I * 2
-    bytes_ = active * 2 * I * H * wb + x_read + h_write
+    bytes_ = int(active * 2 * I * H * wb) + x_read + h_write
     flops = 4.0 * T * k * H * I
     return bytes_, flops
 
@@ -106,9 +112,9 @@ def layer_work(cfg, active):
     """Algorithmic bytes and flops of the whole block (weights of active
     experts + x + out + router weight; expert and router flops)."""
     T, H, I, k, E = cfg["T"], cfg["hidden"], cfg["intermediate"], cfg["top_k"], cfg["n_experts"]
-    wb = 1 if cfg["w_dtype"] == "fp8" else 2
+    wb = WEIGHT_BYTES[cfg["w_dtype"]]
     xb = 4 if cfg["x_dtype"] == "f32" else 2
-    bytes_ = active * 3 * I * H * wb + 2 * T * H * xb + E * H * 4
+    bytes_ = int(active * 3 * I * H * wb) + 2 * T * H * xb + E * H * 4
     flops = 6.0 * T * k * H * I
     return bytes_, flops
 
@@ -156,12 +162,15 @@ class Bench:
         self.x, self.rw, self.b = x.to(dev), rw.to(dev), b.to(dev)
         self.w = weights if weights is not None else workloads.make_expert_weights(cfg, 0, dev)
         # the MFMA fragment copy the timed forward reads (packed once, at load)
+        mx = self.w["w_gate"].dtype == torch.uint8
         self.pw = packed if packed is not None else {
             k: gl.pack_weights(self.w[k]) for k in ("w_gate", "w_up", "w_down")}
         w = self.w
         self.scales = None
         if w["w_gate"].dtype == torch.float8_e4m3fn:
             self.scales = (w["w_gate_scale"], w["w_up_scale"], w["w_down_scale"])
+        elif mx:  # MXFP4: the block scales are packed like the codes
+            self.scales = tuple(gl.pack_mx_scales(w[k + "_scale"]) for k in ("w_gate", "w_up", "w_down"))
         xdt = self.x.dtype
         wdt = w["w_gate"].dtype
         c = gl.make_config(cfg["hidden"], cfg["intermediate"], cfg["n_experts"], cfg["n_group"],
@@ -222,14 +231,18 @@ def cpu_baseline(cfg, bench, n_tokens):
     r = oracle.route(x64, rw64, b64, cfg["n_group"], cfg["topk_group"], cfg["top_k"])
     need = sorted(set(int(e) for e in np.unique(r["idx"])))
     fp8 = cfg["w_dtype"] == "fp8"
+    mx = cfg["w_dtype"] == "mxfp4"
     host = {}
     for e in need:  # copy the needed experts to host memory before timing
         host[e] = {k: bench.w[k][e].cpu() for k in ("w_gate", "w_up", "w_down")}
-        if fp8:
+        if fp8 or mx:
             for k in ("w_gate", "w_up", "w_down"):
                 host[e][k + "_scale"] = bench.w[k + "_scale"][e].cpu()
 
     def get(e):
+        if mx:
+            return tuple(oracle.mxfp4.dequantize(host[e][k].numpy(), host[e][k + "_scale"].numpy())
+                         for k in ("w_gate", "w_up", "w_down"))
         if fp8:
             return tuple(oracle.e4m3.decode(host[e][k].view(torch.uint8).numpy())
                          * host[e][k + "_scale"].double().numpy()[:, None]
@@ -239,7 +252,7 @@ def cpu_baseline(cfg, bench, n_tokens):
     t0 = time.perf_counter()
     oracle.forward_tokens(tok, bench.x.cpu().double().numpy(), rw64, b64, get,
                           n_group=cfg["n_group"], topk_group=cfg["topk_group"], top_k=cfg["top_k"],
-                          routed_scaling_factor=cfg["routed_scaling_factor"], fp8=fp8)
+                          routed_scaling_factor=cfg["routed_scaling_factor"], fp8=fp8 or mx)
     dt = time.perf_counter() - t0
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s",
             "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
@@ -329,7 +342,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skewed", "fp8"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "prefill", "skewed", "fp8", "mxfp4"])
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -364,7 +378,7 @@ def main():
     cfg = workloads.workload(args.workload)
     bench = Bench(cfg, dev)
     res = bench.run(args.steps, args.warmup)
-    wdt = "fp8" if cfg["w_dtype"] == "fp8" else "bf16"
+    wdt = "fp8" if cfg["w_dtype"] in ("fp8", "mxfp4") else "bf16"
     gb, gf = gateup_work(cfg, bench.active)
     rl = roofline(gb, gf, res["gateup_ms"] / 1e3, wdt, stored_traffic(cfg["name"]))
     lb, lf = layer_work(cfg, bench.active)
@@ -380,7 +394,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wdt,
+        "dtype": "mxfp4 x e4m3" if cfg["w_dtype"] == "mxfp4" else wdt,
         "data": "synthetic",
         "config": {"workload": describe(cfg), "T": cfg["T"], "hidden": cfg["hidden"],
                    "intermediate": cfg["intermediate"], "n_experts": cfg["n_experts"],

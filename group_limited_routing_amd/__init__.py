@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libbeam_moe.so")
 
 BEAM_OK, BEAM_ERR_NULL, BEAM_ERR_CONFIG, BEAM_ERR_SHAPE = 0, 1, 2, 3
 BEAM_ERR_DTYPE, BEAM_ERR_ALIGN, BEAM_ERR_WORKSPACE, BEAM_ERR_HIP = 4, 5, 6, 7
-BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
+BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3, BEAM_MXFP4, BEAM_E8M0 = 0, 1, 2, 3, 4
 BEAM_LAYOUT_ROW_MAJOR, BEAM_LAYOUT_PACKED = 0, 1
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_forward",
@@ -89,7 +89,9 @@ def status_string(status):
 
 
 _X_DTYPES = {torch.float32: BEAM_F32, torch.bfloat16: BEAM_BF16}
-_W_DTYPES = {torch.bfloat16: BEAM_BF16, torch.float8_e4m3fn: BEAM_FP8_E4M3}
+# uint8 weight tensors are MXFP4 codes (two E2M1 values per byte)
+_W_DTYPES = {torch.bfloat16: BEAM_BF16, torch.float8_e4m3fn: BEAM_FP8_E4M3,
+             torch.uint8: BEAM_MXFP4}
 
 
 def make_config(hidden, intermediate, n_experts=256, n_group=8, topk_group=4, top_k=8,
@@ -104,14 +106,31 @@ def make_config(hidden, intermediate, n_experts=256, n_group=8, topk_group=4, to
 
 def pack_weights(w, out=None, stream=None):
     """MFMA-fragment copy of row-major expert weights w [E, R, C] (bf16 or
-    float8_e4m3fn); pass the result to forward(..., packed=True)."""
+    float8_e4m3fn; uint8 = MXFP4 codes [E, R, C/2]); pass the result to
+    forward(..., packed=True)."""
     if w.dim() != 3 or not w.is_contiguous() or w.dtype not in _W_DTYPES:
-        raise ValueError("pack_weights needs a contiguous [E, rows, cols] bf16/fp8 tensor")
+        raise ValueError("pack_weights needs a contiguous [E, rows, cols] bf16/fp8/MXFP4 tensor")
     if out is None:
         out = torch.empty_like(w)
     E, R, C = w.shape
+    if w.dtype == torch.uint8:
+        C *= 2  # weights per row
     st = lib().beam_moe_pack_weights(_ptr(w), _ptr(out), E, R, C, _W_DTYPES[w.dtype],
                                      _stream(w.device, stream))
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_pack_weights")
+    return out
+
+
+def pack_mx_scales(s, out=None, stream=None):
+    """Packed copy of row-major MXFP4 scale bytes s [E, R, C/32] (uint8, E8M0)."""
+    if s.dim() != 3 or not s.is_contiguous() or s.dtype != torch.uint8:
+        raise ValueError("pack_mx_scales needs a contiguous [E, rows, cols/32] uint8 tensor")
+    if out is None:
+        out = torch.empty_like(s)
+    E, R, B = s.shape
+    st = lib().beam_moe_pack_weights(_ptr(s), _ptr(out), E, R, 32 * B, BEAM_E8M0,
+                                     _stream(s.device, stream))
     if st != BEAM_OK:
         raise BeamMoeError(st, "beam_moe_pack_weights")
     return out
@@ -176,28 +195,37 @@ def forward(x, router_w, expert_bias, w_gate, w_up, w_down, *, scales=None, n_gr
             topk_group=4, top_k=8, routed_scaling_factor=2.5, out=None, return_routing=False,
             return_logits=False, workspace=None, stream=None, packed=False):
     """The whole MoE block. ``scales`` = (w_gate_scale, w_up_scale, w_down_scale)
-    for fp8 weights; ``packed`` says the weights come from pack_weights().
+    for fp8 weights (fp32 per row) and MXFP4 weights (uint8 codes, with the
+    E8M0 block scales from pack_mx_scales); ``packed`` says the weights come
+    from pack_weights() (required for MXFP4).
     Returns out [T, H] (x's dtype), or (out, routing dict) with
     ``return_routing`` or ``return_logits``."""
     T, H = x.shape
     E = router_w.shape[0]
     I = w_gate.shape[1]
     dev = x.device
-    wdt = (torch.bfloat16, torch.float8_e4m3fn)
+    wdt = (torch.bfloat16, torch.float8_e4m3fn, torch.uint8)
+    mx = w_gate.dtype == torch.uint8
+    d = 2 if mx else 1  # MXFP4: two codes per byte
     _check(x, "x", (T, H), (torch.float32, torch.bfloat16), dev)
     _check(router_w, "router_w", (E, H), (torch.float32,), dev)
     _check(expert_bias, "expert_bias", (E,), (torch.float32,), dev)
-    _check(w_gate, "w_gate", (E, I, H), wdt, dev)
-    _check(w_up, "w_up", (E, I, H), (w_gate.dtype,), dev)
-    _check(w_down, "w_down", (E, H, I), (w_gate.dtype,), dev)
+    _check(w_gate, "w_gate", (E, I, H // d), wdt, dev)
+    _check(w_up, "w_up", (E, I, H // d), (w_gate.dtype,), dev)
+    _check(w_down, "w_down", (E, H, I // d), (w_gate.dtype,), dev)
     sg = su = sd = None
-    if w_gate.dtype == torch.float8_e4m3fn:
+    if w_gate.dtype in (torch.float8_e4m3fn, torch.uint8):
         if scales is None:
-            raise ValueError("fp8 weights need (w_gate_scale, w_up_scale, w_down_scale)")
+            raise ValueError("quantised weights need (w_gate_scale, w_up_scale, w_down_scale)")
         sg, su, sd = scales
-        _check(sg, "w_gate_scale", (E, I), (torch.float32,), dev)
-        _check(su, "w_up_scale", (E, I), (torch.float32,), dev)
-        _check(sd, "w_down_scale", (E, H), (torch.float32,), dev)
+        if mx:
+            _check(sg, "w_gate_scale", (E, I, H // 32), (torch.uint8,), dev)
+            _check(su, "w_up_scale", (E, I, H // 32), (torch.uint8,), dev)
+            _check(sd, "w_down_scale", (E, H, I // 32), (torch.uint8,), dev)
+        else:
+            _check(sg, "w_gate_scale", (E, I), (torch.float32,), dev)
+            _check(su, "w_up_scale", (E, I), (torch.float32,), dev)
+            _check(sd, "w_down_scale", (E, H), (torch.float32,), dev)
     cfg = make_config(H, I, E, n_group, topk_group, top_k, routed_scaling_factor, x.dtype,
                       w_gate.dtype, packed)
     if out is None:

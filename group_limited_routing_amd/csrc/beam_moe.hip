@@ -84,11 +84,14 @@ beam_status check_config(const beam_moe_config* c) {
   if (c->top_k < 1 || c->top_k > 32 || c->top_k > c->topk_group * gs) return BEAM_ERR_CONFIG;
   if (!isfinite(c->routed_scaling_factor)) return BEAM_ERR_CONFIG;
   if (c->x_dtype != BEAM_F32 && c->x_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
-  if (c->w_dtype != BEAM_BF16 && c->w_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
+  if (c->w_dtype != BEAM_BF16 && c->w_dtype != BEAM_FP8_E4M3 && c->w_dtype != BEAM_MXFP4)
+    return BEAM_ERR_DTYPE;
   if (c->w_layout != BEAM_LAYOUT_ROW_MAJOR && c->w_layout != BEAM_LAYOUT_PACKED)
     return BEAM_ERR_CONFIG;
-  if (c->hidden <= 0 || c->hidden % 128 != 0 || c->hidden > 65536) return BEAM_ERR_SHAPE;
-  if (c->intermediate <= 0 || c->intermediate % 128 != 0 || c->intermediate > 65536)
+  if (c->w_dtype == BEAM_MXFP4 && c->w_layout != BEAM_LAYOUT_PACKED) return BEAM_ERR_CONFIG;
+  const int step = c->w_dtype == BEAM_MXFP4 ? 512 : 128;
+  if (c->hidden <= 0 || c->hidden % step != 0 || c->hidden > 65536) return BEAM_ERR_SHAPE;
+  if (c->intermediate <= 0 || c->intermediate % step != 0 || c->intermediate > 65536)
     return BEAM_ERR_SHAPE;
   return BEAM_OK;
 }
@@ -104,7 +107,9 @@ Shape shape_of(const beam_moe_config* c, int32_t T) {
   s.top_k = c->top_k;
   s.rsf = c->routed_scaling_factor;
   s.x_f32 = c->x_dtype == BEAM_F32;
-  s.w_fp8 = c->w_dtype == BEAM_FP8_E4M3;
+  // fp8 and MXFP4 weights share the E4M3 activation path
+  s.w_fp8 = c->w_dtype == BEAM_FP8_E4M3 || c->w_dtype == BEAM_MXFP4;
+  s.w_mx4 = c->w_dtype == BEAM_MXFP4;
   s.w_packed = c->w_layout == BEAM_LAYOUT_PACKED;
   return s;
 }
@@ -283,8 +288,8 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
 
 beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x,
                              const float* router_w, const float* expert_bias, const void* w_gate,
-                             const void* w_up, const void* w_down, const float* w_gate_scale,
-                             const float* w_up_scale, const float* w_down_scale, void* out,
+                             const void* w_up, const void* w_down, const void* w_gate_scale,
+                             const void* w_up_scale, const void* w_down_scale, void* out,
                              int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
                              float* router_logits_out, void* workspace, size_t workspace_bytes,
                              void* stream) {
@@ -293,7 +298,7 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
   if (T < 0 || T > kMaxT) return BEAM_ERR_SHAPE;
   if (T == 0) return BEAM_OK;
   if (!x || !router_w || !expert_bias || !w_gate || !w_up || !w_down || !out) return BEAM_ERR_NULL;
-  const bool fp8 = cfg->w_dtype == BEAM_FP8_E4M3;
+  const bool fp8 = cfg->w_dtype == BEAM_FP8_E4M3 || cfg->w_dtype == BEAM_MXFP4;
   if (fp8 && (!w_gate_scale || !w_up_scale || !w_down_scale)) return BEAM_ERR_DTYPE;
   if (!workspace) return BEAM_ERR_WORKSPACE;
   if (misaligned(x) || misaligned(router_w) || misaligned(expert_bias) || misaligned(w_gate) ||
@@ -312,7 +317,7 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
   int32_t* idx = topk_idx_out ? topk_idx_out : B.idx;
   float* w = topk_w_out ? topk_w_out : B.w;
   const int k = s.top_k;
-  const int BM = use_stream_gemm(s) ? kStreamBM : (s.w_packed ? wide_bm(s) : kTiledBM);
+  const int BM = (use_stream_gemm(s) || s.w_mx4) ? kStreamBM : (s.w_packed ? wide_bm(s) : kTiledBM);
 
   const beam_status rs = route_tokens(s, L, B, x, router_w, expert_bias, router_logits_out, idx, w,
                                       st);
@@ -346,8 +351,8 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
     g.a_scale = xs;
     g.w0 = w_gate;
     g.w1 = w_up;
-    g.ws0 = w_gate_scale;
-    g.ws1 = w_up_scale;
+    g.ws0 = (const float*)w_gate_scale;
+    g.ws1 = (const float*)w_up_scale;
     g.out = hf;
     g.hamax = hamax;
     g.K = s.H;
@@ -358,7 +363,7 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
     g.a_scale = hs;
     g.w0 = w_down;
     g.w1 = nullptr;
-    g.ws0 = w_down_scale;
+    g.ws0 = (const float*)w_down_scale;
     g.ws1 = nullptr;
     g.out = y;
     g.hamax = nullptr;
@@ -389,16 +394,25 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
 beam_status beam_moe_pack_weights(const void* src, void* dst, int32_t n_experts, int32_t rows,
                                   int32_t cols, int32_t w_dtype, void* stream) {
   if (!src || !dst) return BEAM_ERR_NULL;
-  if (w_dtype != BEAM_BF16 && w_dtype != BEAM_FP8_E4M3) return BEAM_ERR_DTYPE;
-  if (n_experts < 1 || rows < 16 || rows % 16 != 0 || cols < 128 || cols % 128 != 0)
+  if (w_dtype != BEAM_BF16 && w_dtype != BEAM_FP8_E4M3 && w_dtype != BEAM_MXFP4 &&
+      w_dtype != BEAM_E8M0)
+    return BEAM_ERR_DTYPE;
+  const bool mx = w_dtype == BEAM_MXFP4 || w_dtype == BEAM_E8M0;
+  const int step = mx ? 512 : 128;
+  if (n_experts < 1 || rows < 16 || rows % 16 != 0 || cols < step || cols % step != 0)
     return BEAM_ERR_SHAPE;
   const long long bytes = (long long)n_experts * rows * cols * (w_dtype == BEAM_BF16 ? 2 : 1);
   if (bytes > (1LL << 40)) return BEAM_ERR_SHAPE;
   if (misaligned(src) || misaligned(dst)) return BEAM_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
-  return launch_pack(src, dst, n_experts, rows, cols, w_dtype == BEAM_FP8_E4M3, st) == hipSuccess
-             ? BEAM_OK
-             : BEAM_ERR_HIP;
+  hipError_t err;
+  if (w_dtype == BEAM_E8M0)
+    err = launch_pack_mx_scales((const uint8_t*)src, (uint8_t*)dst, n_experts, rows, cols, st);
+  else if (w_dtype == BEAM_MXFP4)  // 64 bytes of codes per row per 128-column step
+    err = launch_pack_bytes(src, dst, n_experts, rows, cols / 2, 64, st);
+  else
+    err = launch_pack(src, dst, n_experts, rows, cols, w_dtype == BEAM_FP8_E4M3, st);
+  return err == hipSuccess ? BEAM_OK : BEAM_ERR_HIP;
 }
 
 beam_status beam_moe_profile_begin(uint32_t stage_mask) {

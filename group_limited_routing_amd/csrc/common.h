@@ -68,6 +68,15 @@ __device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
 }
 
+// 16x16x128 MFMA with an E4M3 first operand (unit scale) and an OCP MXFP4
+// second operand: lane l holds 32 E2M1 codes (16 bytes, two per byte, low
+// nibble first, in the first four registers of b) of column l % 16 and
+// reduction elements 32 (l / 16) .. + 31, and bscale (low byte) is the E8M0
+// scale of exactly those 32 elements.
+__device__ __forceinline__ f32x4 mfma_fp8_fp4(i32x8 a, i32x8 b, int bscale, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 0x7f7f7f7f, 0, bscale);
+}
+
 // fp32 -> OCP E4M3 code, round to nearest even, finite overflow saturates to
 // +-448, NaN -> 0x7F. Written from the format: bias 7, 3 mantissa bits,
 // subnormal spacing 2^-9, no infinity, largest finite 1.75 * 2^8.

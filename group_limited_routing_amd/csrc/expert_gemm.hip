@@ -312,6 +312,135 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------- MXFP4 stream variant
+// Expert GEMMs with MXFP4 weights (packed: one 1 KB block per 16 rows x 128
+// reduction steps, two E2M1 codes per byte; E8M0 block scales packed so that
+// one 4-byte load gives a lane the scales of four consecutive steps). The
+// token rows are E4M3 codes with a per-row fp32 scale (applied in the
+// epilogue); each 16x16x128 MFMA takes the weight fragment as its second
+// operand together with the lane's block scale. Same M-tiles, waves and
+// register ring as the streaming bf16/fp8 variant.
+template <int MODE, int FN, int D>
+__global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
+  constexpr int HALF = FN / 2;
+  constexpr int COLS_W = (MODE == 0) ? 16 * HALF : 16 * FN;  // output columns per wave
+  constexpr int COLS = 4 * COLS_W;                           // per workgroup
+  const int ntn = p.N / COLS;
+  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  TileInfo ti;
+  if (!tile_info(p, mt, kStreamBM, ti)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N;
+
+  // Padded rows (r >= rows) repeat the last real row; their results are not stored.
+  const int ar = min(r, ti.rows - 1);
+  const uint8_t* arow = (MODE == 0) ? (const uint8_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K + 32 * g
+                                    : (const uint8_t*)p.a + (size_t)(ti.row0 + ar) * K + 32 * g;
+  const int ncol0 = nt * COLS + wave * COLS_W;
+  const uint8_t* brow[FN];   // this lane's 16 code bytes of step 0
+  const uint32_t* srow[FN];  // this lane's scale dword of steps 0..3
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const bool up = MODE == 0 && f >= HALF;
+    const int n = (MODE == 0) ? ncol0 + (f % HALF) * 16 + r : ncol0 + f * 16 + r;
+    const int rb = (n - r) >> 4;
+    const uint8_t* W = (const uint8_t*)(up ? p.w1 : p.w0);
+    const uint32_t* S = (const uint32_t*)(up ? p.ws1 : p.ws0);
+    brow[f] = W + (size_t)ti.e * N * (K / 2) + (size_t)rb * 8 * K + lane * 16;
+    srow[f] = S + ((size_t)ti.e * (N / 16) + rb) * (K / 512) * 64 + lane;
+  }
+
+  f32x4 acc[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nks = K / 128;  // a multiple of 4
+  Op32 aq[D];
+  u32x4 bq[D][FN];
+  uint32_t sq[D][FN];
+  auto load_step = [&](int d, int s) {
+    aq[d] = load_op<true>(arow + (size_t)s * 128);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      bq[d][f] = ld16(brow[f] + (size_t)s * 1024);
+      sq[d][f] = srow[f][(s >> 2) * 64] >> (8 * (s & 3));
+    }
+  };
+  auto consume = [&](int d) {
+    i32x8 a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = (int)aq[d].lo[i];
+      a[4 + i] = (int)aq[d].hi[i];
+    }
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      i32x8 b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        b[i] = (int)bq[d][f][i];
+        b[4 + i] = 0;
+      }
+      acc[f] = mfma_fp8_fp4(a, b, (int)(sq[d][f] & 0xffu), acc[f]);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_step(d, min(d, nks - 1));
+  int s0 = 0;
+  for (; s0 + 2 * D <= nks; s0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      consume(d);
+      load_step(d, s0 + d + D);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (s0 + d < nks) {
+      consume(d);
+      if (s0 + d + D < nks) load_step(d, s0 + d + D);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (s0 + D + d < nks) consume(d);
+
+  if (MODE == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g + i;
+      const bool valid = row < ti.rows;
+      const float xs = valid ? p.a_scale[p.stok[ti.row0 + row]] : 0.f;
+      float rowmax = 0.f;
+#pragma unroll
+      for (int f = 0; f < HALF; ++f) {
+        const int n = ncol0 + f * 16 + r;
+        if (valid) {
+          const float h = silu_f32(acc[f][i] * xs) * (acc[f + HALF][i] * xs);
+          ((float*)p.out)[(size_t)(ti.row0 + row) * N + n] = h;
+          rowmax = fmaxf(rowmax, fabsf(h));
+        }
+      }
+      row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
+    }
+  } else {
+    uint16_t* out = (uint16_t*)p.out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g + i;
+      if (row < ti.rows) {
+        const float rs = p.a_scale[ti.row0 + row] * p.sw[ti.row0 + row];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          const int n = ncol0 + f * 16 + r;
+          out[(size_t)(ti.row0 + row) * N + n] = (uint16_t)f32_to_bf16_bits(acc[f][i] * rs);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- tiled variant
 // An LDS tile row holds 128 bytes of k (64 bf16 or 128 fp8 values) as eight
 // 16-byte chunks; chunk c of row r lives at chunk position c ^ (r & 7), so the
@@ -1161,8 +1290,20 @@ static void launch_variant(const Shape& s, const GemmArgs& g, hipStream_t st) {
   }
 }
 
+// MXFP4 weights: the streaming variant at every batch size. Hidden and
+// intermediate are multiples of 512, so 8 fragments per wave always divide.
+template <int MODE>
+static void launch_stream4(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  constexpr int FN = 8, D = 2;
+  constexpr int per = (MODE == 0) ? 4 * 16 * FN / 2 : 4 * 16 * FN;
+  dim3 grid(mtile_bound(s, kStreamBM) * (g.N / per));
+  gemm_stream4_kernel<MODE, FN, D><<<grid, 256, 0, st>>>(g);
+}
+
 hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st) {
-  if (s.w_fp8)
+  if (s.w_mx4)
+    launch_stream4<0>(s, g, st);
+  else if (s.w_fp8)
     launch_variant<0, uint8_t, true>(s, g, st);
   else if (s.x_f32)
     launch_variant<0, float, false>(s, g, st);
@@ -1172,7 +1313,9 @@ hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st) {
 }
 
 hipError_t launch_down(const Shape& s, const GemmArgs& g, hipStream_t st) {
-  if (s.w_fp8)
+  if (s.w_mx4)
+    launch_stream4<1>(s, g, st);
+  else if (s.w_fp8)
     launch_variant<1, uint8_t, true>(s, g, st);
   else
     launch_variant<1, uint16_t, false>(s, g, st);
@@ -1201,6 +1344,45 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ s
   const long long row = rb * 16 + (lane & 15);
   const long long kb = (long long)st * SB + (lane >> 4) * LB + j;
   st16(dst + o, ld16(src + e * mat_bytes + row * row_bytes + kb));
+}
+
+hipError_t launch_pack_bytes(const void* src, void* dst, int E, int rows, int row_bytes, int SB,
+                             hipStream_t st) {
+  const long long mat = (long long)rows * row_bytes;
+  const long long chunks = (long long)E * mat / 16;
+  const long long blocks = (chunks + 255) / 256;
+  pack_kernel<<<(unsigned)blocks, 256, 0, st>>>((const uint8_t*)src, (uint8_t*)dst, chunks, mat,
+                                                row_bytes, SB);
+  return hipGetLastError();
+}
+
+// MXFP4 scale bytes, row-major [E, rows, cols / 32] -> packed: the dword of
+// (row block rb, step group q, lane l) holds, in byte j, the scale of row
+// 16 rb + l % 16 and column block 16 q + 4 j + l / 16 (step 4 q + j).
+__global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __restrict__ src,
+                                                             uint32_t* __restrict__ dst,
+                                                             long long dwords, int rows, int cols) {
+  const long long d = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (d >= dwords) return;
+  const int nb = cols / 32, nq = cols / 512;
+  const int lane = (int)(d & 63);
+  long long t = d >> 6;
+  const int q = (int)(t % nq);
+  t /= nq;
+  const int rb = (int)(t % (rows / 16));
+  const long long e = t / (rows / 16);
+  const long long row = (long long)rb * 16 + (lane & 15);
+  const uint8_t* sr = src + (e * rows + row) * nb + 16 * q + (lane >> 4);
+  dst[d] = (uint32_t)sr[0] | ((uint32_t)sr[4] << 8) | ((uint32_t)sr[8] << 16) |
+           ((uint32_t)sr[12] << 24);
+}
+
+hipError_t launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, int E, int rows, int cols,
+                                 hipStream_t st) {
+  const long long dwords = (long long)E * rows * (cols / 32) / 4;
+  pack_mx_scales_kernel<<<(unsigned)((dwords + 255) / 256), 256, 0, st>>>(src, (uint32_t*)dst, dwords,
+                                                                          rows, cols);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const void* src, void* dst, int E, int rows, int cols, int fp8,

@@ -17,6 +17,7 @@ struct Shape {
   int x_f32;   // 1: x/out fp32, 0: bf16
   int w_fp8;   // 1: fp8 e4m3 weights with per-row scales
   int w_packed;  // 1: weights in the MFMA fragment layout
+  int w_mx4;     // 1: MXFP4 weights (w_fp8 is set too: E4M3 activations)
 };
 
 // Byte offsets of each workspace region (all 256-byte aligned).
@@ -78,6 +79,11 @@ hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st);
 hipError_t launch_down(const Shape& s, const GemmArgs& g, hipStream_t st);
 hipError_t launch_pack(const void* src, void* dst, int E, int rows, int cols, int fp8,
                        hipStream_t st);
+// rows of row_bytes bytes, SB bytes per row per matrix-core step
+hipError_t launch_pack_bytes(const void* src, void* dst, int E, int rows, int row_bytes, int SB,
+                             hipStream_t st);
+hipError_t launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, int E, int rows, int cols,
+                                 hipStream_t st);
 hipError_t launch_combine(const void* y, const int32_t* inv, int T, int k, int H, int out_f32,
                           void* out, hipStream_t st);
 hipError_t launch_quant_x(const void* x, int x_f32, int T, int H, int k, uint8_t* xq, float* xs,

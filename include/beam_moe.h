@@ -60,7 +60,12 @@ typedef enum beam_status {
 typedef enum beam_dtype {
   BEAM_F32 = 0,      /* IEEE binary32 */
   BEAM_BF16 = 1,     /* bfloat16 (upper 16 bits of binary32) */
-  BEAM_FP8_E4M3 = 2  /* OCP FP8 E4M3 ("e4m3fn"): bias 7, no infinity, max 448 */
+  BEAM_FP8_E4M3 = 2, /* OCP FP8 E4M3 ("e4m3fn"): bias 7, no infinity, max 448 */
+  BEAM_MXFP4 = 3,    /* OCP MXFP4: E2M1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3,
+                        4, 6; sign in bit 3), two per byte with element 2j in
+                        the low nibble, plus one E8M0 scale byte (value
+                        2^(code - 127)) per 32 consecutive elements of a row */
+  BEAM_E8M0 = 4      /* the MXFP4 scale bytes (beam_moe_pack_weights only) */
 } beam_dtype;
 
 /*
@@ -75,11 +80,13 @@ typedef enum beam_dtype {
  *   n_group a power of two in [1, 64] (groups of 256 / n_group >= 4 experts);
  *   1 <= topk_group <= n_group;
  *   1 <= top_k <= min(32, topk_group * 256 / n_group);
- *   hidden and intermediate positive multiples of 128, each <= 65536;
+ *   hidden and intermediate positive multiples of 128, each <= 65536
+ *   (multiples of 512 with BEAM_MXFP4 weights);
  *   routed_scaling_factor finite;
  *   x_dtype in {BEAM_F32, BEAM_BF16} (the output has the same dtype);
- *   w_dtype in {BEAM_BF16, BEAM_FP8_E4M3};
- *   w_layout in {BEAM_LAYOUT_ROW_MAJOR, BEAM_LAYOUT_PACKED}.
+ *   w_dtype in {BEAM_BF16, BEAM_FP8_E4M3, BEAM_MXFP4};
+ *   w_layout in {BEAM_LAYOUT_ROW_MAJOR, BEAM_LAYOUT_PACKED} (BEAM_MXFP4:
+ *   BEAM_LAYOUT_PACKED only).
  */
 typedef struct beam_moe_config {
   int32_t hidden;
@@ -108,6 +115,14 @@ typedef struct beam_moe_config {
  *     contiguous block (1 KB bf16, 2 KB fp8) in the order the 64 lanes of a
  *     wavefront consume it. Same size as row-major; the per-row fp8 scales
  *     keep their [n_experts, R] layout.
+ *     MXFP4 codes use S = 128 and L = 32 with two codes per byte (each block
+ *     is 1 KB: lane l's 16 bytes hold the 32 codes of row r % 16, columns
+ *     32 (l / 16) .. + 31 of the step). Their scale bytes (row-major
+ *     [n_experts, R, C / 32]) are packed as well: the scale of row r, column
+ *     block b = c / 32 goes to byte
+ *       ((r / 16) * (C / 512) + b / 16) * 256 + ((r % 16) + 16 * (b % 4)) * 4
+ *         + (b % 16) / 4,
+ *     so one 4-byte load gives a lane the scales of four consecutive steps.
  */
 typedef enum beam_layout {
   BEAM_LAYOUT_ROW_MAJOR = 0,
@@ -148,13 +163,18 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
  *   w_gate, w_up  [n_experts, intermediate, hidden] (each expert's matrix is
  *                 [out, in] row-major), w_dtype.
  *   w_down        [n_experts, hidden, intermediate], w_dtype.
- *   w_gate_scale, w_up_scale  [n_experts, intermediate] fp32 and
- *   w_down_scale  [n_experts, hidden] fp32: per-output-row dequantisation
- *                 scales (the weight is code * scale). Required when w_dtype is
- *                 BEAM_FP8_E4M3, ignored (may be NULL) otherwise.
- *                 With fp8 weights the expert inputs are quantised to E4M3 per
- *                 row as well: x per token, the SwiGLU output per (token,
- *                 expert) row, each with scale amax / 448.
+ *   w_gate_scale, w_up_scale, w_down_scale  dequantisation scales, required
+ *                 with quantised weights, ignored (may be NULL) with bf16:
+ *                 BEAM_FP8_E4M3: fp32, [n_experts, intermediate] (gate, up)
+ *                 and [n_experts, hidden] (down), one per output row (the
+ *                 weight is code * scale);
+ *                 BEAM_MXFP4: the packed E8M0 scale bytes (see beam_layout),
+ *                 one per 32 weights of a row.
+ *                 With fp8 or MXFP4 weights the expert inputs are quantised
+ *                 to E4M3 per row: x per token, the SwiGLU output per (token,
+ *                 expert) row, each with scale amax / 448. MXFP4 weights run
+ *                 the streaming expert kernels at every batch size (the
+ *                 decode regime, where their bytes are the cost).
  *   out           out [T, hidden], x_dtype.
  *   topk_idx_out  out [T, top_k] int32 or NULL; topk_w_out out [T, top_k] fp32
  *                 or NULL; expert_counts_out out [n_experts] int32 or NULL;
@@ -167,23 +187,25 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
 beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x,
                              const float* router_w, const float* expert_bias,
                              const void* w_gate, const void* w_up, const void* w_down,
-                             const float* w_gate_scale, const float* w_up_scale,
-                             const float* w_down_scale, void* out, int32_t* topk_idx_out,
+                             const void* w_gate_scale, const void* w_up_scale,
+                             const void* w_down_scale, void* out, int32_t* topk_idx_out,
                              float* topk_w_out, int32_t* expert_counts_out,
                              float* router_logits_out, void* workspace, size_t workspace_bytes,
                              void* stream);
 
 /*
- * Convert n_experts row-major [rows, cols] weight matrices (w_dtype BEAM_BF16
- * or BEAM_FP8_E4M3) at `src` into BEAM_LAYOUT_PACKED at `dst` (same byte
- * size), on `stream`. A one-time transform at weight-load time: the packed
- * layout lets every matrix-core operand load of the expert GEMMs read one
- * contiguous block. src and dst are caller-owned device memory, 16-byte
- * aligned, and must not overlap.
+ * Convert n_experts row-major [rows, cols] weight matrices at `src` into
+ * BEAM_LAYOUT_PACKED at `dst` (same byte size), on `stream`. w_dtype:
+ * BEAM_BF16 or BEAM_FP8_E4M3 (the matrices), BEAM_MXFP4 (the code matrices,
+ * cols / 2 bytes per row) or BEAM_E8M0 (their scale bytes, cols / 32 per
+ * row); cols is always the number of weights per row. A one-time transform
+ * at weight-load time: the packed layout lets every matrix-core operand load
+ * of the expert GEMMs read one contiguous block. src and dst are
+ * caller-owned device memory, 16-byte aligned, and must not overlap.
  * Errors: BEAM_ERR_NULL (src or dst NULL), BEAM_ERR_SHAPE (n_experts < 1,
- * rows not a positive multiple of 16, cols not a positive multiple of 128,
- * or more than 2^40 bytes in all), BEAM_ERR_DTYPE, BEAM_ERR_ALIGN,
- * BEAM_ERR_HIP (launch failed).
+ * rows not a positive multiple of 16, cols not a positive multiple of 128
+ * (512 for BEAM_MXFP4 and BEAM_E8M0), or more than 2^40 bytes in all),
+ * BEAM_ERR_DTYPE, BEAM_ERR_ALIGN, BEAM_ERR_HIP (launch failed).
  */
 beam_status beam_moe_pack_weights(const void* src, void* dst, int32_t n_experts, int32_t rows,
                                   int32_t cols, int32_t w_dtype, void* stream);

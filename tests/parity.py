@@ -29,18 +29,25 @@ def f64(t):
     return t.detach().to("cpu", torch.float64).numpy() if t.dtype != torch.float8_e4m3fn else None
 
 
+def is_mxfp4(w):
+    return w["w_gate"].dtype == torch.uint8
+
+
 def packed_copy(w):
-    """The same weights in the MFMA fragment layout (made by the library)."""
+    """The same weights in the MFMA fragment layout (made by the library);
+    MXFP4 scale bytes are packed too."""
     pw = dict(w)
     for k in ("w_gate", "w_up", "w_down"):
         pw[k] = gl.pack_weights(w[k])
+        if is_mxfp4(w):
+            pw[k + "_scale"] = gl.pack_mx_scales(w[k + "_scale"])
     pw["packed"] = True
     return pw
 
 
 def run_forward(x, rw, b, w, cfg, **kw):
     scales = None
-    if w["w_gate"].dtype == torch.float8_e4m3fn:
+    if w["w_gate"].dtype in (torch.float8_e4m3fn, torch.uint8):
         scales = (w["w_gate_scale"], w["w_up_scale"], w["w_down_scale"])
     out, r = gl.forward(x, rw, b, w["w_gate"], w["w_up"], w["w_down"], scales=scales,
                         packed=w.get("packed", False),
@@ -53,14 +60,18 @@ def run_forward(x, rw, b, w, cfg, **kw):
 
 def expert_getter(w):
     """get_expert(e) for the oracle: one expert copied to the host, float64
-    (fp8 weights dequantised with their per-row scales)."""
+    (fp8 weights dequantised with their per-row scales, MXFP4 weights with
+    their block scales; the row-major copies)."""
     fp8 = w["w_gate"].dtype == torch.float8_e4m3fn
+    mx = is_mxfp4(w)
 
     def get(e):
         mats = []
         for k in ("w_gate", "w_up", "w_down"):
             m = w[k][e].to("cpu")
-            if fp8:
+            if mx:
+                mats.append(oracle.mxfp4.dequantize(m.numpy(), w[k + "_scale"][e].to("cpu").numpy()))
+            elif fp8:
                 codes = m.view(torch.uint8).numpy()
                 sc = w[k + "_scale"][e].to("cpu").numpy().astype(np.float64)
                 mats.append(oracle.e4m3.decode(codes) * sc[:, None])
@@ -138,7 +149,8 @@ def oracle_reference(tokens, x, rw, b, w, cfg, gpu_idx, near):
     forced = r["idx"].copy()
     nt = near[tokens]
     forced[nt] = gpu_idx[tokens][nt]
-    fp8 = w["w_gate"].dtype == torch.float8_e4m3fn
+    # fp8 and MXFP4 weights: the expert inputs are E4M3-quantised per row
+    fp8 = w["w_gate"].dtype in (torch.float8_e4m3fn, torch.uint8)
     out, _ = oracle.forward(x64[tokens], rw64, b64, expert_getter(w), cfg["n_group"],
                             cfg["topk_group"], cfg["top_k"], cfg["routed_scaling_factor"],
                             routing=forced, fp8=fp8)

@@ -114,6 +114,27 @@ def test_fp8_needs_scales(L):
     assert _fwd(L, c, 8, sg=FAKE, su=FAKE, sd=FAKE + 4) == gl.BEAM_ERR_ALIGN
 
 
+def test_mxfp4_checks(L):
+    """MXFP4 weights: packed layout only, hidden and intermediate multiples of
+    512, block scales required; packing needs 512-weight rows."""
+    mx = gl.BEAM_MXFP4
+    assert _fwd(L, beam_cfg(w_dtype=mx), 8) == gl.BEAM_ERR_CONFIG            # row-major
+    ok = beam_cfg(w_dtype=mx, w_layout=gl.BEAM_LAYOUT_PACKED)
+    assert _fwd(L, ok, 8) == gl.BEAM_ERR_DTYPE                                 # no scales
+    assert _fwd(L, ok, 8, sg=FAKE, su=FAKE, sd=FAKE + 8) == gl.BEAM_ERR_ALIGN
+    for kw in [dict(hidden=5120 - 128), dict(intermediate=2560 + 256)]:
+        c = beam_cfg(w_dtype=mx, w_layout=gl.BEAM_LAYOUT_PACKED, **kw)
+        assert _fwd(L, c, 8, sg=FAKE, su=FAKE, sd=FAKE) == gl.BEAM_ERR_SHAPE, kw
+    f = gl.workspace_bytes(beam_cfg(w_dtype=gl.BEAM_FP8_E4M3), 64)
+    assert gl.workspace_bytes(ok, 64) == f  # the E4M3 activation buffers of the fp8 path
+    v = ctypes.c_void_p
+    pk = L.beam_moe_pack_weights
+    for dt in (gl.BEAM_MXFP4, gl.BEAM_E8M0):
+        assert pk(v(FAKE), v(FAKE), 256, 2560, 5120 - 128, dt, None) == gl.BEAM_ERR_SHAPE
+        assert pk(v(FAKE), v(FAKE), 256, 2568, 5120, dt, None) == gl.BEAM_ERR_SHAPE
+    assert pk(v(FAKE), v(FAKE), 256, 2560, 5120, 5, None) == gl.BEAM_ERR_DTYPE
+
+
 def test_workspace_size(L):
     c = beam_cfg()
     need = gl.workspace_bytes(c, 64)
@@ -159,6 +180,7 @@ def test_library_links_every_kernel(L):
     syms = subprocess.run([nm, "-C", gl.LIB_PATH], capture_output=True, text=True, check=True).stdout
     for kernel in ["router_logits_kernel", "router_split_kernel", "router_x3_kernel", "select_kernel", "perm_hist_kernel", "perm_scan_kernel",
                    "perm_scatter_kernel", "gemm_stream_kernel", "gemm_tiled_kernel",
-                   "gemm_wide_kernel", "gemm_dma_kernel", "gemm_dma8_kernel", "combine_kernel", "quant_x_kernel",
+                   "gemm_wide_kernel", "gemm_dma_kernel", "gemm_dma8_kernel", "gemm_stream4_kernel",
+                   "combine_kernel", "pack_mx_scales_kernel", "quant_x_kernel",
                    "quant_h_kernel", "pack_kernel"]:
         assert f"__device_stub__{kernel}" in syms, kernel

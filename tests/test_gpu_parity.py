@@ -138,6 +138,35 @@ def test_fp8_dma_variant_256_rows():
     _full_compare("fp8 dma 256", cfg, 16, True)
 
 
+def test_mxfp4_stream_variant():
+    cfg = _case(200, 512, 1024, w_dtype="mxfp4")   # ragged M-tiles, 4-bit weights
+    _full_compare("mxfp4 stream", cfg, 18, True)
+
+
+def test_mxfp4_many_rows_per_expert():
+    # ~47 rows per expert: MXFP4 stays on the streaming kernels (3 M-tiles each)
+    cfg = _case(1500, 1024, 512, w_dtype="mxfp4")
+    _full_compare("mxfp4 many rows", cfg, 19, True)
+
+
+def test_mxfp4_pack_layouts():
+    """Packed MXFP4 codes and scale bytes equal their documented layouts,
+    built here with torch views (an independent formulation)."""
+    dev = _dev()
+    E, R, C = 2, 32, 1024
+    g = torch.Generator(device=dev).manual_seed(3)
+    codes = torch.randint(0, 256, (E, R, C // 2), generator=g, device=dev, dtype=torch.uint8)
+    sc = torch.randint(0, 256, (E, R, C // 32), generator=g, device=dev, dtype=torch.uint8)
+    pc, ps = gl.pack_weights(codes), gl.pack_mx_scales(sc)
+    torch.cuda.synchronize()
+    # codes: 128 weights (64 bytes) per row per step, lane l = r % 16 + 16 * (chunk of 16 bytes)
+    ref = codes.view(E, R // 16, 16, C // 128, 4, 16).permute(0, 1, 3, 4, 2, 5).contiguous()
+    assert torch.equal(pc.view(-1), ref.view(-1))
+    # scales: block b of row r -> ((r/16)*(C/512) + b/16)*256 + (r%16 + 16*(b%4))*4 + (b%16)/4
+    ref = sc.view(E, R // 16, 16, C // 512, 4, 4).permute(0, 1, 3, 5, 2, 4).contiguous()
+    assert torch.equal(ps.view(-1), ref.view(-1))
+
+
 @pytest.mark.parametrize("dtype,S", [(torch.bfloat16, 32), (torch.float8_e4m3fn, 128)])
 def test_pack_layout_matches_definition(dtype, S):
     """The packed copy equals the documented layout, built here with a torch
@@ -296,6 +325,19 @@ def test_beam_skewed_full_shape(beam_bf16_weights, beam_bf16_packed, packed):
         assert int(cnt.sum()) == 8 * 16384
     w, ow = _pick(packed, beam_bf16_weights, beam_bf16_packed)
     _full_shape("skewed T=16384" + (" packed" if packed else ""), "skewed", w, skewed, ow)
+
+
+def test_beam_mxfp4_decode_full_shape():
+    dev = _dev()
+    cfg = workloads.workload("mxfp4")
+    w = workloads.make_expert_weights(cfg, 0, dev)
+    pw = packed_copy(w)
+    torch.cuda.synchronize()
+    try:
+        _full_shape("mxfp4 decode T=64 packed", "mxfp4", pw, oracle_weights=w)
+    finally:
+        del w, pw
+        torch.cuda.empty_cache()
 
 
 def test_beam_fp8_full_shape():

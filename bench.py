@@ -347,7 +347,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens the oracle runs on (default: 64, MXFP4 weights 4; ~10-30 s)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -427,7 +428,8 @@ def main():
         }
         del pb
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, bench, min(args.cpu_tokens, cfg["T"]))
+        n_cpu = args.cpu_tokens or (4 if cfg["w_dtype"] == "mxfp4" else 64)
+        line["cpu_baseline"] = cpu_baseline(cfg, bench, min(n_cpu, cfg["T"]))
     print(json.dumps(line), flush=True)
     return 0
 

@@ -334,9 +334,16 @@ __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
   const int K = p.K, N = p.N;
 
   // Padded rows (r >= rows) repeat the last real row; their results are not stored.
+  // With an fp4 second operand the instruction pairs the 32 codes of weight
+  // lane group g (reduction elements 32 g .. + 31 of the step) with bytes
+  // 0-15 of activation lane groups 2 (g % 2) and 2 (g % 2) + 1 ... in this
+  // arrangement: activation lane group g holds elements 16 g .. + 15 in its
+  // first 16 bytes and 64 + 16 g .. + 15 in its last 16 (measured on gfx950
+  // with one-hot operands), so that each weight lane's 32 codes, and its one
+  // block scale, meet their own 32 activations.
   const int ar = min(r, ti.rows - 1);
-  const uint8_t* arow = (MODE == 0) ? (const uint8_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K + 32 * g
-                                    : (const uint8_t*)p.a + (size_t)(ti.row0 + ar) * K + 32 * g;
+  const uint8_t* arow = (MODE == 0) ? (const uint8_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K + 16 * g
+                                    : (const uint8_t*)p.a + (size_t)(ti.row0 + ar) * K + 16 * g;
   const int ncol0 = nt * COLS + wave * COLS_W;
   const uint8_t* brow[FN];   // this lane's 16 code bytes of step 0
   const uint32_t* srow[FN];  // this lane's scale dword of steps 0..3
@@ -360,7 +367,8 @@ __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
   u32x4 bq[D][FN];
   uint32_t sq[D][FN];
   auto load_step = [&](int d, int s) {
-    aq[d] = load_op<true>(arow + (size_t)s * 128);
+    aq[d].lo = ld16(arow + (size_t)s * 128);
+    aq[d].hi = ld16(arow + (size_t)s * 128 + 64);
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
       bq[d][f] = ld16(brow[f] + (size_t)s * 1024);

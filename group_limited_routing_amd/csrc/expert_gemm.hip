@@ -334,13 +334,13 @@ __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
   const int K = p.K, N = p.N;
 
   // Padded rows (r >= rows) repeat the last real row; their results are not stored.
-  // With an fp4 second operand the instruction pairs the 32 codes of weight
-  // lane group g (reduction elements 32 g .. + 31 of the step) with bytes
-  // 0-15 of activation lane groups 2 (g % 2) and 2 (g % 2) + 1 ... in this
-  // arrangement: activation lane group g holds elements 16 g .. + 15 in its
-  // first 16 bytes and 64 + 16 g .. + 15 in its last 16 (measured on gfx950
-  // with one-hot operands), so that each weight lane's 32 codes, and its one
-  // block scale, meet their own 32 activations.
+  // With an fp4 second operand the instruction pairs codes 0-15 of weight
+  // lane group g with activation lane group 2 (g % 2) and codes 16-31 with
+  // group 2 (g % 2) + 1, in activation bytes 0-15 for g < 2 and 16-31 for
+  // g >= 2 (measured on gfx950 with one-hot operands). Activation lane group
+  // a therefore holds step elements 16 a .. + 15 in bytes 0-15 and
+  // 64 + 16 a .. + 15 in bytes 16-31: each weight lane (32 consecutive
+  // elements, one block scale) then meets exactly its own 32 activations.
   const int ar = min(r, ti.rows - 1);
   const uint8_t* arow = (MODE == 0) ? (const uint8_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K + 16 * g
                                     : (const uint8_t*)p.a + (size_t)(ti.row0 + ar) * K + 16 * g;

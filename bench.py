@@ -65,7 +65,9 @@ def gateup_kernel(cfg):
     xt = "float" if cfg["x_dtype"] == "f32" else "unsigned short"
     fp8 = cfg["w_dtype"] == "fp8"
     if cfg["w_dtype"] == "mxfp4":
-        return "gemm_stream4_kernel<0, 8, 2>"
+        if pairs <= 16 * cfg["n_experts"]:
+            return "gemm_stream4_kernel<0, 8, 2>"
+        return f"gemm_dma4_kernel<0, {256 if pairs >= 96 * cfg['n_experts'] else 128}>"
     if pairs <= 16 * cfg["n_experts"]:
         return f"gemm_stream_kernel<0, {'unsigned char' if fp8 else xt}, {str(fp8).lower()}, true, ...>"
     dma = fp8 or xt == "unsigned short"
@@ -343,7 +345,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "prefill", "skewed", "fp8", "mxfp4"])
+                    choices=["tiny", "decode", "prefill", "skewed", "fp8", "mxfp4", "mxfp4_prefill"])
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -317,7 +317,7 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
   int32_t* idx = topk_idx_out ? topk_idx_out : B.idx;
   float* w = topk_w_out ? topk_w_out : B.w;
   const int k = s.top_k;
-  const int BM = (use_stream_gemm(s) || s.w_mx4) ? kStreamBM : (s.w_packed ? wide_bm(s) : kTiledBM);
+  const int BM = use_stream_gemm(s) ? kStreamBM : (s.w_packed ? wide_bm(s) : kTiledBM);
 
   const beam_status rs = route_tokens(s, L, B, x, router_w, expert_bias, router_logits_out, idx, w,
                                       st);

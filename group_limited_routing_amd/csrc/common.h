@@ -77,6 +77,13 @@ __device__ __forceinline__ f32x4 mfma_fp8_fp4(i32x8 a, i32x8 b, int bscale, f32x
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 0x7f7f7f7f, 0, bscale);
 }
 
+// The same instruction with the operands the other way round: the MXFP4
+// weights (with their per-lane E8M0 scales) as the first operand, E4M3 as
+// the second, so the output holds weight rows along its row dimension.
+__device__ __forceinline__ f32x4 mfma_fp4_fp8(i32x8 a, i32x8 b, int ascale, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, ascale, 0, 0x7f7f7f7f);
+}
+
 // fp32 -> OCP E4M3 code, round to nearest even, finite overflow saturates to
 // +-448, NaN -> 0x7F. Written from the format: bias 7, 3 mantissa bits,
 // subnormal spacing 2^-9, no infinity, largest finite 1.75 * 2^8.

@@ -638,7 +638,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
 // columns 16 c(fn) + 4 g .. + 3, where c(fn) is the fragment's column block:
 // gate/up: fn < FN / 2 gate and fn + FN / 2 the matching up block,
 // c = (FN / 2) wn + fn; down: c = FN wn + fn.
-template <int MODE, bool FP8, int FM, int FN>
+template <int MODE, bool FP8, int FM, int FN, bool BLOCK_SCALED = false>
 __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const TileInfo& ti,
                                                     const f32x4 (&acc)[FM][FN], int row_base,
                                                     int n0, int wn, int r, int g) {
@@ -649,7 +649,7 @@ __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const Til
 #pragma unroll
   for (int fn = 0; fn < NF; ++fn) {
     cs0[fn] = cs1[fn] = f32x4{1.f, 1.f, 1.f, 1.f};
-    if constexpr (FP8) {
+    if constexpr (FP8 && !BLOCK_SCALED) {  // MXFP4: the block scales act inside the MFMA
       const int n = n0 + (wn * NF + fn) * 16 + 4 * g;
       const size_t c = (size_t)ti.e * N + n;
       cs0[fn] = __builtin_bit_cast(f32x4, ld16(p.ws0 + c));
@@ -1211,6 +1211,203 @@ void gemm_dma8_kernel(GemmArgs p) {
   transposed_epilogue<MODE, true, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
 }
 
+// ---------------------------------------------------------------- MXFP4 DMA variant
+// Large batches with MXFP4 weights: the fp8 DMA variant's tiles, waves, tile
+// order and half-stage ring, with the scaled fp8 x fp4 MFMA. A half-stage
+// holds 64 bytes of every A row (chunk g of row r at position
+// g ^ ((r >> 1) & 3)) and half of each of the 16 weight row blocks' 1 KB
+// fragment blocks (lanes 0-31 or 32-63). Activation lane group a takes
+// chunk a of both halves of its step (elements 16 a .. and 64 + 16 a ..),
+// the order in which the instruction pairs it with whole 32-element weight
+// lanes (see the streaming variant; the pairing is the same with the weights
+// as the first operand, which gives the transposed output tile the epilogue
+// expects). The E8M0 block scales of the tile's 16
+// row blocks for four steps (4 KB) go to LDS by DMA at the first two
+// half-stages of the previous four steps (double buffered); those extra
+// loads only ever make the ring's wait counts stricter.
+template <int MODE, int BM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_dma4_kernel(GemmArgs p) {
+  constexpr int A_BYTES = BM * 64, B_BYTES = 16 * 512, STAGE = A_BYTES + B_BYTES;
+  constexpr int SC_BYTES = 16 * 256;            // scales of 16 row blocks x 4 steps
+  constexpr int NS0 = (150 * 1024 - 2 * SC_BYTES) / STAGE;
+  constexpr int NS = NS0 > 8 ? 8 : NS0;         // 5 (BM 256) or 8 (BM 128) slots
+  constexpr int AHEAD = NS - 2;
+  constexpr int FM = BM / 32, FN = 4;
+  constexpr int COLS = (MODE == 0) ? 128 : 256;
+  constexpr int AI = BM / 128;
+  static_assert(AHEAD >= 2, "ring too small");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + 2 * SC_BYTES];
+  uint8_t* scb = smem + NS * STAGE;
+
+  const int ntn = p.N / COLS;
+  const int n_tiles = p.meta[0] * ntn;
+  const int b = blockIdx.x;
+  if (b >= n_tiles) return;
+  const int xcd = b & 7, per = n_tiles >> 3, extra = n_tiles & 7;
+  const int j = xcd * per + min(xcd, extra) + (b >> 3);
+  const int e = p.tile_e[j / ntn];
+  const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
+  const int jj = j - ts * ntn;
+  const int mb = jj / (kGroupM * ntn), rem = jj - mb * kGroupM * ntn;
+  const int gm = min(kGroupM, nm - mb * kGroupM);
+  const int nt = rem / gm, mt = ts + mb * kGroupM + rem % gm;
+  TileInfo ti;
+  ti.e = e;
+  ti.row0 = p.tile_r[mt];
+  ti.rows = min(BM, p.offsets[e + 1] - ti.row0);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3, r = lane & 15, g = lane >> 4;
+  const int K = p.K, N = p.N;
+  const int n0 = nt * COLS;
+
+  // A: as in the fp8 DMA variant.
+  const uint8_t* asrc[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = (wave * AI + i) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    const int ar = min(row, ti.rows - 1);
+    const uint8_t* base = (MODE == 0) ? (const uint8_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K
+                                      : (const uint8_t*)p.a + (size_t)(ti.row0 + ar) * K;
+    asrc[i] = base + chunk * 16;
+  }
+  // B: one instruction per wave and half-stage: lanes 0-31 load half h of
+  // row block 2 wave, lanes 32-63 half h of row block 2 wave + 1.
+  const uint8_t* bsrc;
+  {
+    const int rbk = wave * 2 + (lane >> 5);
+    const uint8_t* W = (const uint8_t*)((MODE == 0 && rbk >= 8) ? p.w1 : p.w0);
+    const int blk = (MODE == 0) ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
+    bsrc = W + (size_t)ti.e * N * (K / 2) + (size_t)blk * 8 * K + (lane & 31) * 16;
+  }
+  // Scales: in half-stage 8 q + i (i = 0, 1) wave w loads the dwords of steps
+  // 4 (q + 1) .. + 3 of local row block 2 w + i (64 lanes x 4 bytes).
+  const uint32_t* ssrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rbk = wave * 2 + i;
+    const uint32_t* S = (const uint32_t*)((MODE == 0 && rbk >= 8) ? p.ws1 : p.ws0);
+    const int blk = (MODE == 0) ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
+    ssrc[i] = S + ((size_t)ti.e * (N / 16) + blk) * (K / 512) * 64 + lane;
+  }
+  auto scale_dma = [&](int grp, int i) {  // step group grp of local row block 2 wave + i
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(ssrc[i] + (size_t)grp * 64,
+                                     scb + (grp & 1) * SC_BYTES + (wave * 2 + i) * 256, 4, 0, 0);
+#endif
+  };
+  auto issue = [&](int hs, auto al_c) {
+    constexpr int AL = decltype(al_c)::value;
+    uint8_t* st = smem + (hs % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < AL; ++i) dma16(asrc[i] + (size_t)hs * 64, st + (wave * AI + i) * 1024);
+    dma16(bsrc + (size_t)(hs >> 1) * 1024 + (hs & 1) * 512, st + A_BYTES + wave * 1024);
+  };
+
+  // Operand offsets: A chunk g of this lane's row (both halves of the step),
+  // B: this lane's 16 bytes in half lane / 32 of its row block's block.
+  const int half = lane >> 5;
+  int aoff[FM], boff[FN], soff[FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f) {
+    const int row = wm * (BM / 2) + f * 16 + r;
+    aoff[f] = row * 64 + ((g ^ ((row >> 1) & 3)) << 4);
+  }
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const int rbl = (MODE == 0) ? ((f < 2) ? wn * 2 + f : 8 + wn * 2 + (f - 2)) : wn * 4 + f;
+    boff[f] = A_BYTES + rbl * 512 + (lane & 31) * 16;
+    soff[f] = rbl * 256 + lane * 4;
+  }
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nh = K / 64;  // a multiple of 8
+  auto kloop = [&](auto nf_c, auto al_c) {
+    constexpr int NF = decltype(nf_c)::value;
+    constexpr int PER = decltype(al_c)::value + 1;  // A and B DMAs per half-stage
+    scale_dma(0, 0);  // step group 0
+    scale_dma(0, 1);
+#pragma unroll
+    for (int s0 = 0; s0 < AHEAD; ++s0)
+      if (s0 < nh) issue(s0, al_c);
+    for (int hs = 0; hs < nh; ++hs) {
+      if (hs + AHEAD - 1 < nh)
+        wait_vmcnt<(AHEAD - 1) * PER>();
+      else
+        wait_vmcnt<0>();
+      barrier_only();
+      asm volatile("" ::: "memory");
+      if (hs + AHEAD < nh) issue(hs + AHEAD, al_c);
+      // scales of the next step group, at the first two half-stages of a
+      // group: the buffer they fill was last read by the previous group,
+      // whose reads every wave retired before this barrier; they are read
+      // from half-stage 8 (q + 1) + 1 on, whose wait retires them first
+      if ((hs & 7) < 2 && ((hs >> 3) + 1) * 8 < nh) scale_dma((hs >> 3) + 1, hs & 7);
+      if constexpr (NF > 0) {
+        if (hs & 1) {
+          const int s = hs >> 1;
+          const uint8_t* st0 = smem + ((hs - 1) % NS) * STAGE;
+          const uint8_t* st1 = smem + (hs % NS) * STAGE;
+          const uint8_t* stb = half ? st1 : st0;
+          const uint8_t* sc = scb + ((s >> 2) & 1) * SC_BYTES;
+          i32x8 bfr[FN];
+          int bsc[FN];
+#pragma unroll
+          for (int f = 0; f < FN; ++f) {
+            const u32x4 v = ld16(stb + boff[f]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              bfr[f][i] = (int)v[i];
+              bfr[f][4 + i] = 0;
+            }
+            bsc[f] = (int)((*reinterpret_cast<const uint32_t*>(sc + soff[f]) >> (8 * (s & 3))) & 0xffu);
+          }
+#pragma unroll
+          for (int i = 0; i < NF; ++i) {
+            const u32x4 lo = ld16(st0 + aoff[i]), hi = ld16(st1 + aoff[i]);
+            i32x8 a;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              a[q] = (int)lo[q];
+              a[4 + q] = (int)hi[q];
+            }
+#pragma unroll
+            for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_fp4_fp8(bfr[jn], a, bsc[jn], acc[i][jn]);
+          }
+        }
+      }
+      wait_lgkmcnt0();
+      asm volatile("" ::: "memory");
+    }
+  };
+  const int need = min(FM, max(0, (ti.rows - wm * (BM / 2) + 15) >> 4));
+  const int al = min(AI, max(0, (ti.rows - wave * AI * 16 + 15) >> 4));
+  auto run = [&](auto nf_c) {
+    if (al == 0)
+      kloop(nf_c, std::integral_constant<int, 0>{});
+    else if (al == 1)
+      kloop(nf_c, std::integral_constant<int, 1>{});
+    else
+      kloop(nf_c, std::integral_constant<int, AI>{});
+  };
+  if (need == 0)
+    run(std::integral_constant<int, 0>{});
+  else if (need <= FM / 4)
+    run(std::integral_constant<int, FM / 4>{});
+  else if (need <= FM / 2)
+    run(std::integral_constant<int, FM / 2>{});
+  else
+    run(std::integral_constant<int, FM>{});
+
+  transposed_epilogue<MODE, true, FM, FN, true>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
+}
+
 // ---------------------------------------------------------------- launchers
 int mtile_bound(const Shape& s, int BM) {
   const long long pairs = (long long)s.T * s.top_k;
@@ -1298,19 +1495,30 @@ static void launch_variant(const Shape& s, const GemmArgs& g, hipStream_t st) {
   }
 }
 
-// MXFP4 weights: the streaming variant at every batch size. Hidden and
-// intermediate are multiples of 512, so 8 fragments per wave always divide.
+// MXFP4 weights: the streaming variant for decode-sized batches (hidden and
+// intermediate are multiples of 512, so 8 fragments per wave always divide),
+// the DMA variant beyond.
 template <int MODE>
-static void launch_stream4(const Shape& s, const GemmArgs& g, hipStream_t st) {
-  constexpr int FN = 8, D = 2;
-  constexpr int per = (MODE == 0) ? 4 * 16 * FN / 2 : 4 * 16 * FN;
-  dim3 grid(mtile_bound(s, kStreamBM) * (g.N / per));
-  gemm_stream4_kernel<MODE, FN, D><<<grid, 256, 0, st>>>(g);
+static void launch_mx4(const Shape& s, const GemmArgs& g, hipStream_t st) {
+  if (use_stream_gemm(s)) {
+    constexpr int FN = 8, D = 2;
+    constexpr int per = (MODE == 0) ? 4 * 16 * FN / 2 : 4 * 16 * FN;
+    dim3 grid(mtile_bound(s, kStreamBM) * (g.N / per));
+    gemm_stream4_kernel<MODE, FN, D><<<grid, 256, 0, st>>>(g);
+    return;
+  }
+  const int BM = wide_bm(s);
+  long long n = (long long)mtile_bound(s, BM) * (g.N / (MODE == 0 ? 128 : 256));
+  n = (n + 7) & ~7LL;
+  if (BM == 256)
+    gemm_dma4_kernel<MODE, 256><<<(unsigned)n, 512, 0, st>>>(g);
+  else
+    gemm_dma4_kernel<MODE, 128><<<(unsigned)n, 512, 0, st>>>(g);
 }
 
 hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st) {
   if (s.w_mx4)
-    launch_stream4<0>(s, g, st);
+    launch_mx4<0>(s, g, st);
   else if (s.w_fp8)
     launch_variant<0, uint8_t, true>(s, g, st);
   else if (s.x_f32)
@@ -1322,7 +1530,7 @@ hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st) {
 
 hipError_t launch_down(const Shape& s, const GemmArgs& g, hipStream_t st) {
   if (s.w_mx4)
-    launch_stream4<1>(s, g, st);
+    launch_mx4<1>(s, g, st);
   else if (s.w_fp8)
     launch_variant<1, uint8_t, true>(s, g, st);
   else

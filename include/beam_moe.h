@@ -172,9 +172,7 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
  *                 one per 32 weights of a row.
  *                 With fp8 or MXFP4 weights the expert inputs are quantised
  *                 to E4M3 per row: x per token, the SwiGLU output per (token,
- *                 expert) row, each with scale amax / 448. MXFP4 weights run
- *                 the streaming expert kernels at every batch size (the
- *                 decode regime, where their bytes are the cost).
+ *                 expert) row, each with scale amax / 448.
  *   out           out [T, hidden], x_dtype.
  *   topk_idx_out  out [T, top_k] int32 or NULL; topk_w_out out [T, top_k] fp32
  *                 or NULL; expert_counts_out out [n_experts] int32 or NULL;

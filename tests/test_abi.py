@@ -178,7 +178,7 @@ def test_library_links_every_kernel(L):
                          text=True, check=True).stdout
     assert "beam::" not in und, [ln for ln in und.splitlines() if "beam::" in ln]
     syms = subprocess.run([nm, "-C", gl.LIB_PATH], capture_output=True, text=True, check=True).stdout
-    for kernel in ["router_logits_kernel", "router_split_kernel", "router_x3_kernel", "select_kernel", "perm_hist_kernel", "perm_scan_kernel",
+    for kernel in ["gemm_dma4_kernel", "router_logits_kernel", "router_split_kernel", "router_x3_kernel", "select_kernel", "perm_hist_kernel", "perm_scan_kernel",
                    "perm_scatter_kernel", "gemm_stream_kernel", "gemm_tiled_kernel",
                    "gemm_wide_kernel", "gemm_dma_kernel", "gemm_dma8_kernel", "gemm_stream4_kernel",
                    "combine_kernel", "pack_mx_scales_kernel", "quant_x_kernel",

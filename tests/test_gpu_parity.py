@@ -143,10 +143,16 @@ def test_mxfp4_stream_variant():
     _full_compare("mxfp4 stream", cfg, 18, True)
 
 
-def test_mxfp4_many_rows_per_expert():
-    # ~47 rows per expert: MXFP4 stays on the streaming kernels (3 M-tiles each)
+def test_mxfp4_dma_variant_128_rows():
+    # ~47 rows per expert: the MXFP4 DMA variant with 128-row tiles
     cfg = _case(1500, 1024, 512, w_dtype="mxfp4")
-    _full_compare("mxfp4 many rows", cfg, 19, True)
+    _full_compare("mxfp4 dma 128", cfg, 19, True)
+
+
+def test_mxfp4_dma_variant_256_rows():
+    # ~100 rows per expert: 256-row tiles, partly live waves, 4 scale groups
+    cfg = _case(3200, 512, 512, w_dtype="mxfp4")
+    _full_compare("mxfp4 dma 256", cfg, 20, True)
 
 
 def test_mxfp4_pack_layouts():
@@ -335,6 +341,19 @@ def test_beam_mxfp4_decode_full_shape():
     torch.cuda.synchronize()
     try:
         _full_shape("mxfp4 decode T=64 packed", "mxfp4", pw, oracle_weights=w)
+    finally:
+        del w, pw
+        torch.cuda.empty_cache()
+
+
+def test_beam_mxfp4_prefill_full_shape():
+    dev = _dev()
+    cfg = workloads.workload("mxfp4_prefill")
+    w = workloads.make_expert_weights(cfg, 0, dev)
+    pw = packed_copy(w)
+    torch.cuda.synchronize()
+    try:
+        _full_shape("mxfp4 prefill T=4096 packed", "mxfp4_prefill", pw, oracle_weights=w)
     finally:
         del w, pw
         torch.cuda.empty_cache()

@@ -38,6 +38,7 @@ WORKLOADS = {
     "skewed": dict(T=16384, x_dtype="bf16", w_dtype="bf16", bias="hot"),
     "fp8": dict(T=8192, x_dtype="bf16", w_dtype="fp8", bias="normal"),
     "mxfp4": dict(T=64, x_dtype="bf16", w_dtype="mxfp4", bias="normal"),
+    "mxfp4_prefill": dict(T=4096, x_dtype="bf16", w_dtype="mxfp4", bias="balanced"),
 }
 
 DATA_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "data")

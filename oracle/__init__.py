@@ -37,3 +37,4 @@ from .routing import sigmoid, group_scores, select_from_keys, route  # noqa: F40
 from .experts import expert_ffn, forward, forward_tokens, dense_forward  # noqa: F401
 from . import e4m3  # noqa: F401
 from . import mxfp4  # noqa: F401
+from . import residual  # noqa: F401

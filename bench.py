@@ -185,14 +185,27 @@ class Bench:
         cnt = r["expert_counts"].cpu()
         self.active = int((cnt > 0).sum())
         self.max_over_mean = float(cnt.max().item() / cnt.float().mean().item())
+        self.residual = None
+
+    def use_residual(self, step):
+        """Time the block with its fused residual-stream step from now on."""
+        import workloads
+        stream, gain = workloads.make_residual_inputs(self.cfg, 0)
+        dev = self.x.device
+        self.residual = (stream.to(dev), gain.to(dev), step)
 
     def step(self):
         w = self.pw
-        self.gl.forward(self.x, self.rw, self.b, w["w_gate"], w["w_up"], w["w_down"],
-                        scales=self.scales, packed=True, n_group=self.cfg["n_group"],
-                        topk_group=self.cfg["topk_group"], top_k=self.cfg["top_k"],
-                        routed_scaling_factor=self.cfg["routed_scaling_factor"], out=self.out,
-                        workspace=self.ws)
+        kw = dict(scales=self.scales, packed=True, n_group=self.cfg["n_group"],
+                  topk_group=self.cfg["topk_group"], top_k=self.cfg["top_k"],
+                  routed_scaling_factor=self.cfg["routed_scaling_factor"], out=self.out,
+                  workspace=self.ws)
+        if self.residual is None:
+            self.gl.forward(self.x, self.rw, self.b, w["w_gate"], w["w_up"], w["w_down"], **kw)
+        else:
+            s, g, k = self.residual
+            self.gl.forward_residual(self.x, self.rw, self.b, w["w_gate"], w["w_up"],
+                                     w["w_down"], s, g, k, **kw)
 
     def run(self, steps, warmup):
         torch, gl = self.torch, self.gl
@@ -349,6 +362,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-residual", action="store_true",
+                    help="skip timing the block with its fused residual step")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens the oracle runs on (default: 64, MXFP4 weights 4; ~10-30 s)")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -410,6 +425,17 @@ def main():
                   "pct_mfma": round(lf / step_s / 1e12 / MFMA_PEAK_TFLOPS[wdt], 4),
                   "algorithmic_bytes": lb, "flops": lf, "stages_ms": res["stages_ms"]},
     }
+    if not args.no_residual:
+        # the same block with the fused post-norm + depth-scaled residual step
+        # (the MoE of the last layer: step 105)
+        bench.use_residual(105)
+        rres = bench.run(min(args.steps, 50), 3)
+        bench.residual = None
+        line["fused_residual"] = {
+            "step": 105, "ms_per_step": round(rres["ms_per_step"], 4),
+            "value": round(cfg["T"] / (rres["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
+            "combine_ms": rres["stages_ms"].get("combine"),
+            "plain_combine_ms": res["stages_ms"].get("combine")}
     if args.workload == "decode" and not args.no_prefill:
         pcfg = workloads.workload("prefill")
         pb = Bench(pcfg, dev, weights=bench.w, packed=bench.pw)

@@ -24,8 +24,8 @@ BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3, BEAM_MXFP4, BEAM_E8M0 = 0, 1, 2, 3, 4
 BEAM_LAYOUT_ROW_MAJOR, BEAM_LAYOUT_PACKED = 0, 1
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_forward",
-            "beam_moe_status_string", "beam_moe_profile_begin", "beam_moe_profile_end",
-            "beam_moe_pack_weights")
+            "beam_moe_forward_residual", "beam_moe_status_string", "beam_moe_profile_begin",
+            "beam_moe_profile_end", "beam_moe_pack_weights")
 
 STAGES = ("router_logits", "select", "perm_hist", "perm_scan", "perm_scatter", "quant_x",
           "gateup", "quant_h", "down", "combine")
@@ -43,6 +43,15 @@ class BeamMoeConfig(ctypes.Structure):
         ("x_dtype", ctypes.c_int32),
         ("w_dtype", ctypes.c_int32),
         ("w_layout", ctypes.c_int32),
+    ]
+
+
+class BeamMoeResidual(ctypes.Structure):
+    _fields_ = [
+        ("stream_in", ctypes.c_void_p),
+        ("norm_weight", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
+        ("step", ctypes.c_int32),
     ]
 
 
@@ -72,6 +81,10 @@ def lib():
         L.beam_moe_forward.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
         L.beam_moe_forward.restype = ctypes.c_int
+        L.beam_moe_forward_residual.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                ctypes.POINTER(BeamMoeResidual), vp, vp, vp, vp,
+                                                vp, vp, sz, vp]
+        L.beam_moe_forward_residual.restype = ctypes.c_int
         L.beam_moe_status_string.argtypes = [i32]
         L.beam_moe_status_string.restype = ctypes.c_char_p
         L.beam_moe_profile_begin.argtypes = [ctypes.c_uint32]
@@ -200,6 +213,32 @@ def forward(x, router_w, expert_bias, w_gate, w_up, w_down, *, scales=None, n_gr
     from pack_weights() (required for MXFP4).
     Returns out [T, H] (x's dtype), or (out, routing dict) with
     ``return_routing`` or ``return_logits``."""
+    return _forward(x, router_w, expert_bias, w_gate, w_up, w_down, None, scales, n_group,
+                    topk_group, top_k, routed_scaling_factor, out, return_routing,
+                    return_logits, workspace, stream, packed)
+
+
+def forward_residual(x, router_w, expert_bias, w_gate, w_up, w_down, stream_in, norm_weight,
+                     step, *, norm_eps=1e-6, scales=None, n_group=8, topk_group=4, top_k=8,
+                     routed_scaling_factor=2.5, out=None, return_routing=False,
+                     return_logits=False, workspace=None, stream=None, packed=False):
+    """The MoE block and its residual-stream step at sublayer step ``step``:
+    returns sqrt((step-1)/step) * stream_in + RMSNorm(block output) / sqrt(step)
+    (RMSNorm with gain ``norm_weight`` [H] fp32 and ``norm_eps``), x's dtype.
+    ``out`` may be ``stream_in`` itself. Other arguments as for forward()."""
+    T, H = x.shape
+    _check(stream_in, "stream_in", (T, H), (x.dtype,), x.device)
+    _check(norm_weight, "norm_weight", (H,), (torch.float32,), x.device)
+    res = BeamMoeResidual(stream_in.data_ptr(), norm_weight.data_ptr(), float(norm_eps),
+                          int(step))
+    return _forward(x, router_w, expert_bias, w_gate, w_up, w_down, res, scales, n_group,
+                    topk_group, top_k, routed_scaling_factor, out, return_routing,
+                    return_logits, workspace, stream, packed)
+
+
+def _forward(x, router_w, expert_bias, w_gate, w_up, w_down, res, scales, n_group, topk_group,
+             top_k, routed_scaling_factor, out, return_routing, return_logits, workspace,
+             stream, packed):
     T, H = x.shape
     E = router_w.shape[0]
     I = w_gate.shape[1]
@@ -240,12 +279,23 @@ def forward(x, router_w, expert_bias, w_gate, w_up, w_down, *, scales=None, n_gr
     if return_logits:
         logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     ws = _workspace(cfg, T, dev, workspace)
-    st = lib().beam_moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
-                                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sg), _ptr(su),
-                                _ptr(sd), _ptr(out), _ptr(idx), _ptr(w), _ptr(counts),
-                                _ptr(logits), _ptr(ws), ws.numel(), _stream(dev, stream))
+    if res is None:
+        st = lib().beam_moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w),
+                                    _ptr(expert_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                    _ptr(sg), _ptr(su), _ptr(sd), _ptr(out), _ptr(idx), _ptr(w),
+                                    _ptr(counts), _ptr(logits), _ptr(ws), ws.numel(),
+                                    _stream(dev, stream))
+        where = "beam_moe_forward"
+    else:
+        st = lib().beam_moe_forward_residual(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w),
+                                             _ptr(expert_bias), _ptr(w_gate), _ptr(w_up),
+                                             _ptr(w_down), _ptr(sg), _ptr(su), _ptr(sd),
+                                             ctypes.byref(res), _ptr(out), _ptr(idx), _ptr(w),
+                                             _ptr(counts), _ptr(logits), _ptr(ws), ws.numel(),
+                                             _stream(dev, stream))
+        where = "beam_moe_forward_residual"
     if st != BEAM_OK:
-        raise BeamMoeError(st, "beam_moe_forward")
+        raise BeamMoeError(st, where)
     if return_routing or return_logits:
         return out, {"topk_idx": idx, "topk_w": w, "expert_counts": counts,
                      "router_logits": logits}

@@ -286,18 +286,29 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
   return BEAM_OK;
 }
 
-beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x,
-                             const float* router_w, const float* expert_bias, const void* w_gate,
-                             const void* w_up, const void* w_down, const void* w_gate_scale,
-                             const void* w_up_scale, const void* w_down_scale, void* out,
-                             int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
-                             float* router_logits_out, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward pass; with `res` set the final combine is the fused residual step.
+beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
+                         const float* router_w, const float* expert_bias, const void* w_gate,
+                         const void* w_up, const void* w_down, const void* w_gate_scale,
+                         const void* w_up_scale, const void* w_down_scale,
+                         const beam_moe_residual* res, void* out, int32_t* topk_idx_out,
+                         float* topk_w_out, int32_t* expert_counts_out, float* router_logits_out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   const beam_status cs = check_config(cfg);
   if (cs != BEAM_OK) return cs;
   if (T < 0 || T > kMaxT) return BEAM_ERR_SHAPE;
+  if (res) {
+    if (!isfinite(res->norm_eps) || res->norm_eps < 0.f || res->step < 2) return BEAM_ERR_CONFIG;
+    if (cfg->hidden > kResidualMaxH) return BEAM_ERR_SHAPE;
+  }
   if (T == 0) return BEAM_OK;
   if (!x || !router_w || !expert_bias || !w_gate || !w_up || !w_down || !out) return BEAM_ERR_NULL;
+  if (res && (!res->stream_in || !res->norm_weight)) return BEAM_ERR_NULL;
+  if (res && (misaligned(res->stream_in) || misaligned(res->norm_weight))) return BEAM_ERR_ALIGN;
   const bool fp8 = cfg->w_dtype == BEAM_FP8_E4M3 || cfg->w_dtype == BEAM_MXFP4;
   if (fp8 && (!w_gate_scale || !w_up_scale || !w_down_scale)) return BEAM_ERR_DTYPE;
   if (!workspace) return BEAM_ERR_WORKSPACE;
@@ -387,8 +398,46 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
     g.N = s.H;
     STAGE(BEAM_STAGE_DOWN, launch_down(s, g, st));
   }
-  STAGE(BEAM_STAGE_COMBINE, launch_combine(y, B.inv, T, k, s.H, s.x_f32, out, st));
+  if (res) {
+    const double kk = res->step;
+    const float keep = (float)sqrt((kk - 1.0) / kk), add = (float)(1.0 / sqrt(kk));
+    STAGE(BEAM_STAGE_COMBINE, launch_combine_residual(y, B.inv, T, k, s.H, s.x_f32, res->stream_in,
+                                                      res->norm_weight, res->norm_eps, keep, add,
+                                                      out, st));
+  } else {
+    STAGE(BEAM_STAGE_COMBINE, launch_combine(y, B.inv, T, k, s.H, s.x_f32, out, st));
+  }
   return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x,
+                             const float* router_w, const float* expert_bias, const void* w_gate,
+                             const void* w_up, const void* w_down, const void* w_gate_scale,
+                             const void* w_up_scale, const void* w_down_scale, void* out,
+                             int32_t* topk_idx_out, float* topk_w_out, int32_t* expert_counts_out,
+                             float* router_logits_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return forward_impl(cfg, T, x, router_w, expert_bias, w_gate, w_up, w_down, w_gate_scale,
+                      w_up_scale, w_down_scale, nullptr, out, topk_idx_out, topk_w_out,
+                      expert_counts_out, router_logits_out, workspace, workspace_bytes, stream);
+}
+
+beam_status beam_moe_forward_residual(const beam_moe_config* cfg, int32_t T, const void* x,
+                                      const float* router_w, const float* expert_bias,
+                                      const void* w_gate, const void* w_up, const void* w_down,
+                                      const void* w_gate_scale, const void* w_up_scale,
+                                      const void* w_down_scale, const beam_moe_residual* residual,
+                                      void* stream_out, int32_t* topk_idx_out, float* topk_w_out,
+                                      int32_t* expert_counts_out, float* router_logits_out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!residual) return BEAM_ERR_NULL;
+  return forward_impl(cfg, T, x, router_w, expert_bias, w_gate, w_up, w_down, w_gate_scale,
+                      w_up_scale, w_down_scale, residual, stream_out, topk_idx_out, topk_w_out,
+                      expert_counts_out, router_logits_out, workspace, workspace_bytes, stream);
 }
 
 beam_status beam_moe_pack_weights(const void* src, void* dst, int32_t n_experts, int32_t rows,

@@ -1626,6 +1626,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 4
   for (int j = 0; j < k; ++j) {
     const int pos = inv[(size_t)t * k + j];
     const u32x4 q = ld16(y + (size_t)pos * H + c * 8);
@@ -1656,6 +1657,102 @@ hipError_t launch_combine(const void* y, const int32_t* inv, int T, int k, int H
     combine_kernel<1><<<blocks, 256, 0, st>>>((const uint16_t*)y, inv, T, k, H, out);
   else
     combine_kernel<0><<<blocks, 256, 0, st>>>((const uint16_t*)y, inv, T, k, H, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- combine + residual step
+// One workgroup per token. The token's MoE output v (the fp32 sum over its
+// slots, as in combine_kernel) stays in registers, RMS over the hidden
+// dimension by a workgroup reduction, then
+//   out = keep * stream_in + add * (v * rstd * gain),  rstd = 1 / sqrt(mean v^2 + eps).
+// Each thread reads its own stream_in values before writing them, so
+// stream_out may be the same memory as stream_in. 1024 threads per token (a
+// decode batch has few tokens: the width keeps enough loads in flight);
+// kResidualChunks chunks of 8 per thread cover H <= 1024 * 8 * kResidualChunks.
+constexpr int kResidualThreads = 1024;
+constexpr int kResidualChunks = kResidualMaxH / (kResidualThreads * 8);
+
+template <typename XT>
+__global__ __launch_bounds__(kResidualThreads) void combine_residual_kernel(
+    const uint16_t* __restrict__ y, const int32_t* __restrict__ inv, int k, int H,
+    const XT* stream_in, const float* __restrict__ gain, float eps, float keep, float add,
+    XT* stream_out) {
+  constexpr int kWaves = kResidualThreads / 64;
+  __shared__ float red[kWaves];
+  const int t = blockIdx.x, vpr = H / 8;
+  const int32_t* slots = inv + (size_t)t * k;
+  float acc[kResidualChunks][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < kResidualChunks; ++u) {
+    const int c = threadIdx.x + kResidualThreads * u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+    if (c < vpr) {
+#pragma unroll 4
+      for (int j = 0; j < k; ++j) {
+        const u32x4 q = ld16(y + (size_t)slots[j] * H + c * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[u][2 * i] += bf16_bits_to_f32(q[i] & 0xffffu);
+          acc[u][2 * i + 1] += bf16_bits_to_f32(q[i] >> 16);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += acc[u][i] * acc[u][i];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) tot += red[i];
+  const float mean = tot / (float)H;
+  const float rstd = 1.0f / sqrtf(mean + eps);
+  const float scale = add * rstd;
+  const XT* srow = stream_in + (size_t)t * H;
+  XT* orow = stream_out + (size_t)t * H;
+#pragma unroll
+  for (int u = 0; u < kResidualChunks; ++u) {
+    const int c = threadIdx.x + kResidualThreads * u;
+    if (c < vpr) {
+      ALoad16<XT> sv;
+      sv.load(srow + c * 8);
+      float s[8], o[8];
+      sv.floats(s);
+      const u32x4 g0 = ld16(gain + c * 8), g1 = ld16(gain + c * 8 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[i] = keep * s[i] + scale * acc[u][i] * __uint_as_float(g0[i]);
+        o[4 + i] = keep * s[4 + i] + scale * acc[u][4 + i] * __uint_as_float(g1[i]);
+      }
+      if constexpr (sizeof(XT) == 4) {
+        st16(orow + c * 8, u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]),
+                                 __float_as_uint(o[2]), __float_as_uint(o[3])});
+        st16(orow + c * 8 + 4, u32x4{__float_as_uint(o[4]), __float_as_uint(o[5]),
+                                     __float_as_uint(o[6]), __float_as_uint(o[7])});
+      } else {
+        st16(orow + c * 8, u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                 pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])});
+      }
+    }
+  }
+}
+
+hipError_t launch_combine_residual(const void* y, const int32_t* inv, int T, int k, int H,
+                                   int x_f32, const void* stream_in, const float* gain, float eps,
+                                   float keep, float add, void* stream_out, hipStream_t st) {
+  if (H > kResidualMaxH || H % 8) return hipErrorInvalidValue;
+  if (x_f32)
+    combine_residual_kernel<float><<<T, kResidualThreads, 0, st>>>((const uint16_t*)y, inv, k, H,
+                                                      (const float*)stream_in, gain, eps, keep,
+                                                      add, (float*)stream_out);
+  else
+    combine_residual_kernel<uint16_t><<<T, kResidualThreads, 0, st>>>((const uint16_t*)y, inv, k, H,
+                                                         (const uint16_t*)stream_in, gain, eps,
+                                                         keep, add, (uint16_t*)stream_out);
   return hipGetLastError();
 }
 

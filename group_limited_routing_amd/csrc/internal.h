@@ -86,6 +86,12 @@ hipError_t launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, int E, int ro
                                  hipStream_t st);
 hipError_t launch_combine(const void* y, const int32_t* inv, int T, int k, int H, int out_f32,
                           void* out, hipStream_t st);
+// Largest hidden size of the fused combine + residual step (a token's row is
+// held in the registers of one workgroup).
+constexpr int kResidualMaxH = 16384;
+hipError_t launch_combine_residual(const void* y, const int32_t* inv, int T, int k, int H,
+                                   int x_f32, const void* stream_in, const float* gain, float eps,
+                                   float keep, float add, void* stream_out, hipStream_t st);
 hipError_t launch_quant_x(const void* x, int x_f32, int T, int H, int k, uint8_t* xq, float* xs,
                           uint32_t* hamax, hipStream_t st);
 hipError_t launch_quant_h(const float* hf, const uint32_t* hamax, int rows, int I, uint8_t* hq,

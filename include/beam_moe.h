@@ -192,6 +192,40 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
                              void* stream);
 
 /*
+ * The block followed by its place in Beam's residual stream, fused into the
+ * final combine (launch post "Introducing Beam", section "Residual Stream";
+ * model doc "Beam", "Overview": depth-scaled residual and sandwich norm):
+ *   stream_out = sqrt((k-1)/k) * stream_in + RMSNorm(moe_out) / sqrt(k),
+ *   RMSNorm(v) = v / sqrt(mean over hidden of v^2 + norm_eps) * norm_weight,
+ * computed in fp32 per token from the fp32 sum of the expert outputs (the
+ * MoE output itself is never stored). k is this sublayer's step: the input
+ * embedding is step 1, then every attention and MLP sublayer adds one.
+ *   stream_in   [T, hidden], x_dtype; may be the same memory as stream_out.
+ *   norm_weight [hidden] fp32.
+ *   norm_eps    finite, >= 0.
+ *   step        k >= 2.
+ * All other arguments as for beam_moe_forward (stream_out replaces out).
+ * Errors: as beam_moe_forward; BEAM_ERR_NULL if residual, its stream_in or
+ * norm_weight is NULL; BEAM_ERR_CONFIG if step < 2 or norm_eps is negative or
+ * not finite; BEAM_ERR_SHAPE if hidden > 16384 (the row is staged in LDS).
+ */
+typedef struct beam_moe_residual {
+  const void* stream_in;
+  const float* norm_weight;
+  float norm_eps;
+  int32_t step;
+} beam_moe_residual;
+
+beam_status beam_moe_forward_residual(const beam_moe_config* cfg, int32_t T, const void* x,
+                                      const float* router_w, const float* expert_bias,
+                                      const void* w_gate, const void* w_up, const void* w_down,
+                                      const void* w_gate_scale, const void* w_up_scale,
+                                      const void* w_down_scale, const beam_moe_residual* residual,
+                                      void* stream_out, int32_t* topk_idx_out, float* topk_w_out,
+                                      int32_t* expert_counts_out, float* router_logits_out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Convert n_experts row-major [rows, cols] weight matrices at `src` into
  * BEAM_LAYOUT_PACKED at `dst` (same byte size), on `stream`. w_dtype:
  * BEAM_BF16 or BEAM_FP8_E4M3 (the matrices), BEAM_MXFP4 (the code matrices,

@@ -135,6 +135,37 @@ def test_mxfp4_checks(L):
     assert pk(v(FAKE), v(FAKE), 256, 2560, 5120, 5, None) == gl.BEAM_ERR_DTYPE
 
 
+def _fwd_res(L, cfg, T, res, **over):
+    p = dict(x=FAKE, rw=FAKE, b=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, out=FAKE, ws=FAKE)
+    p.update(over)
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.beam_moe_forward_residual(ctypes.byref(cfg), T, v(p["x"]), v(p["rw"]), v(p["b"]),
+                                       v(p["wg"]), v(p["wu"]), v(p["wd"]), None, None, None,
+                                       None if res is None else ctypes.byref(res), v(p["out"]),
+                                       None, None, None, None, v(p["ws"]), 1 << 40, None)
+
+
+def test_residual_checks(L):
+    """The fused residual step: step >= 2, a finite eps >= 0, hidden <= 16384,
+    its two pointers present and aligned; T == 0 still a no-op."""
+    c = beam_cfg()
+    R = lambda **kw: gl.BeamMoeResidual(**dict(dict(stream_in=FAKE, norm_weight=FAKE,
+                                                    norm_eps=1e-6, step=5), **kw))
+    assert _fwd_res(L, c, 8, None) == gl.BEAM_ERR_NULL
+    for kw in [dict(step=1), dict(step=0), dict(step=-3), dict(norm_eps=-1e-6),
+               dict(norm_eps=float("nan")), dict(norm_eps=float("inf"))]:
+        assert _fwd_res(L, c, 8, R(**kw)) == gl.BEAM_ERR_CONFIG, kw
+        assert _fwd_res(L, c, 0, R(**kw)) == gl.BEAM_ERR_CONFIG, kw
+    assert _fwd_res(L, beam_cfg(hidden=16384 + 128), 8, R()) == gl.BEAM_ERR_SHAPE
+    assert _fwd_res(L, c, 8, R(stream_in=None)) == gl.BEAM_ERR_NULL
+    assert _fwd_res(L, c, 8, R(norm_weight=None)) == gl.BEAM_ERR_NULL
+    assert _fwd_res(L, c, 8, R(stream_in=FAKE + 2)) == gl.BEAM_ERR_ALIGN
+    assert _fwd_res(L, c, 8, R(norm_weight=FAKE + 4)) == gl.BEAM_ERR_ALIGN
+    assert _fwd_res(L, c, 8, R(), out=None) == gl.BEAM_ERR_NULL
+    assert _fwd_res(L, c, 0, R(stream_in=None, norm_weight=None), x=None, out=None,
+                    ws=None) == gl.BEAM_OK
+
+
 def test_workspace_size(L):
     c = beam_cfg()
     need = gl.workspace_bytes(c, 64)
@@ -181,6 +212,6 @@ def test_library_links_every_kernel(L):
     for kernel in ["gemm_dma4_kernel", "router_logits_kernel", "router_split_kernel", "router_x3_kernel", "select_kernel", "perm_hist_kernel", "perm_scan_kernel",
                    "perm_scatter_kernel", "gemm_stream_kernel", "gemm_tiled_kernel",
                    "gemm_wide_kernel", "gemm_dma_kernel", "gemm_dma8_kernel", "gemm_stream4_kernel",
-                   "combine_kernel", "pack_mx_scales_kernel", "quant_x_kernel",
+                   "combine_kernel", "combine_residual_kernel", "pack_mx_scales_kernel", "quant_x_kernel",
                    "quant_h_kernel", "pack_kernel"]:
         assert f"__device_stub__{kernel}" in syms, kernel

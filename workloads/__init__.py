@@ -109,6 +109,19 @@ def make_small_inputs(cfg, seed=0):
     return x, router_w, bias
 
 
+def make_residual_inputs(cfg, seed=0):
+    """stream_in [T, H] (x's dtype) and the post-norm gain [H] fp32 (CPU
+    tensors) for the fused residual step. The stream is unit-RMS noise (the
+    scale of a stream of unit-RMS contributions after the depth scaling); the
+    gain is uniform in [0.5, 1.5]."""
+    T, H = cfg["T"], cfg["hidden"]
+    stream = normal((T, H), 1.0, seed, "stream_in")
+    if cfg["x_dtype"] == "bf16":
+        stream = stream.to(torch.bfloat16)
+    g = torch.rand((H,), generator=generator(seed, "norm_weight"), dtype=torch.float32)
+    return stream, g + 0.5
+
+
 # E2M1 magnitudes and the midpoints between neighbours (storage format of the
 # 4-bit checkpoint: OCP MXFP4, blocks of 32 along the reduction dimension).
 _E2M1_MID = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]

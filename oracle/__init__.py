@@ -38,3 +38,4 @@ from .experts import expert_ffn, forward, forward_tokens, dense_forward  # noqa:
 from . import e4m3  # noqa: F401
 from . import mxfp4  # noqa: F401
 from . import residual  # noqa: F401
+from . import backward  # noqa: F401

@@ -13,6 +13,8 @@ import oracle.experts as ox
 import oracle.routing as orr
 from oracle import e4m3
 
+import oracle.backward as ob
+import test_oracle_backward as tb
 import test_oracle_e4m3 as te
 import test_oracle_experts as tx
 import test_oracle_routing as tr
@@ -120,3 +122,26 @@ def test_wrong_exponent_bias_is_caught(monkeypatch):
     real_decode = e4m3.decode
     monkeypatch.setattr(e4m3, "decode", lambda c: real_decode(c) * 2.0)
     assert _fails(te.test_known_codes)
+
+
+def test_backward_silu_derivative_as_sigmoid_is_caught(monkeypatch):
+    monkeypatch.setattr(ob, "dsilu", orr.sigmoid)
+    assert _fails(tb.test_finite_differences_every_parameter)
+    assert _fails(tb.test_matches_torch_autograd, 1)
+
+
+def test_backward_sigmoid_slope_dropped_is_caught(monkeypatch):
+    # the router gradient computed from ds instead of dz (the sigmoid's slope
+    # s (1 - s) left out)
+    real = ob.backward
+
+    def no_slope(x, router_w, *a, **k):
+        out = real(x, router_w, *a, **k)
+        ds_full = np.zeros((out["ds"].shape[0], np.asarray(router_w).shape[0]))
+        np.put_along_axis(ds_full, out["route"]["idx"], out["ds"], axis=1)
+        out["d_router_w"] = ds_full.T @ np.asarray(x)
+        return out
+
+    monkeypatch.setattr(ob, "backward", no_slope)
+    assert _fails(tb.test_finite_differences_every_parameter)
+    assert _fails(tb.test_matches_torch_autograd, 2)

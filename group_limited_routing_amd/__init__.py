@@ -25,10 +25,12 @@ BEAM_LAYOUT_ROW_MAJOR, BEAM_LAYOUT_PACKED = 0, 1
 
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_forward",
             "beam_moe_forward_residual", "beam_moe_status_string", "beam_moe_profile_begin",
-            "beam_moe_profile_end", "beam_moe_pack_weights")
+            "beam_moe_profile_end", "beam_moe_pack_weights", "beam_moe_backward_workspace_bytes",
+            "beam_moe_backward", "beam_moe_pack_weights_transposed", "beam_moe_update_bias")
 
 STAGES = ("router_logits", "select", "perm_hist", "perm_scan", "perm_scatter", "quant_x",
-          "gateup", "quant_h", "down", "combine")
+          "gateup", "quant_h", "down", "combine", "bwd_gateup", "bwd_down", "bwd_dx",
+          "bwd_token", "bwd_router", "bwd_transpose", "bwd_wgrad")
 
 
 class BeamMoeConfig(ctypes.Structure):
@@ -52,6 +54,16 @@ class BeamMoeResidual(ctypes.Structure):
         ("norm_weight", ctypes.c_void_p),
         ("norm_eps", ctypes.c_float),
         ("step", ctypes.c_int32),
+    ]
+
+
+class BeamMoeGrads(ctypes.Structure):
+    _fields_ = [
+        ("dx", ctypes.c_void_p),
+        ("d_router_w", ctypes.c_void_p),
+        ("d_w_gate", ctypes.c_void_p),
+        ("d_w_up", ctypes.c_void_p),
+        ("d_w_down", ctypes.c_void_p),
     ]
 
 
@@ -93,6 +105,15 @@ def lib():
         L.beam_moe_profile_end.restype = ctypes.c_int
         L.beam_moe_pack_weights.argtypes = [vp, vp, i32, i32, i32, i32, vp]
         L.beam_moe_pack_weights.restype = ctypes.c_int
+        L.beam_moe_backward_workspace_bytes.argtypes = [cfgp, i32, i32]
+        L.beam_moe_backward_workspace_bytes.restype = sz
+        L.beam_moe_backward.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        ctypes.POINTER(BeamMoeGrads), vp, sz, vp]
+        L.beam_moe_backward.restype = ctypes.c_int
+        L.beam_moe_pack_weights_transposed.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+        L.beam_moe_pack_weights_transposed.restype = ctypes.c_int
+        L.beam_moe_update_bias.argtypes = [vp, vp, i32, ctypes.c_float, vp]
+        L.beam_moe_update_bias.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -300,6 +321,85 @@ def _forward(x, router_w, expert_bias, w_gate, w_up, w_down, res, scales, n_grou
         return out, {"topk_idx": idx, "topk_w": w, "expert_counts": counts,
                      "router_logits": logits}
     return out
+
+
+def pack_weights_transposed(w, out=None, stream=None):
+    """[E, rows, cols] bf16 expert matrices -> the packed layout of their
+    transposes (what backward() takes as w_gate_t, w_up_t, w_down_t)."""
+    if w.dtype != torch.bfloat16 or w.dim() != 3 or not w.is_contiguous():
+        raise ValueError("expects a contiguous [E, rows, cols] bf16 tensor")
+    E, R, C = w.shape
+    if out is None:
+        out = torch.empty((E, C, R), dtype=w.dtype, device=w.device)
+    st = lib().beam_moe_pack_weights_transposed(_ptr(w), _ptr(out), E, R, C, BEAM_BF16,
+                                                _stream(w.device, stream))
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_pack_weights_transposed")
+    return out
+
+
+def backward_workspace_bytes(cfg, T, weight_grads):
+    return int(lib().beam_moe_backward_workspace_bytes(ctypes.byref(cfg), int(T), int(bool(weight_grads))))
+
+
+def backward(x, router_w, expert_bias, w_gate, w_up, w_gate_t, w_up_t, w_down_t, dout, *,
+             weight_grads=False, router_grad=True, n_group=8, topk_group=4, top_k=8,
+             routed_scaling_factor=2.5, workspace=None, stream=None):
+    """Gradients of sum(dout * forward(...)) (bf16 x and dout, packed bf16
+    weights: w_gate, w_up from pack_weights, the *_t from
+    pack_weights_transposed). Returns dict(dx [T, H] bf16, d_router_w [E, H]
+    fp32 or None, d_w_gate / d_w_up [E, I, H] and d_w_down [E, H, I] bf16
+    with ``weight_grads``, else None)."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    I = w_gate.shape[1]
+    dev = x.device
+    _check(x, "x", (T, H), (torch.bfloat16,), dev)
+    _check(dout, "dout", (T, H), (torch.bfloat16,), dev)
+    _check(router_w, "router_w", (E, H), (torch.float32,), dev)
+    _check(expert_bias, "expert_bias", (E,), (torch.float32,), dev)
+    for name, t, shape in (("w_gate", w_gate, (E, I, H)), ("w_up", w_up, (E, I, H)),
+                           ("w_gate_t", w_gate_t, (E, H, I)), ("w_up_t", w_up_t, (E, H, I)),
+                           ("w_down_t", w_down_t, (E, I, H))):
+        _check(t, name, shape, (torch.bfloat16,), dev)
+    cfg = make_config(H, I, E, n_group, topk_group, top_k, routed_scaling_factor, x.dtype,
+                      torch.bfloat16, packed=True)
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    drw = torch.empty((E, H), dtype=torch.float32, device=dev) if router_grad else None
+    dwg = dwu = dwd = None
+    if weight_grads:
+        dwg = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
+        dwu = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
+        dwd = torch.empty((E, H, I), dtype=torch.bfloat16, device=dev)
+    grads = BeamMoeGrads(dx.data_ptr(), drw.data_ptr() if drw is not None else None,
+                         dwg.data_ptr() if dwg is not None else None,
+                         dwu.data_ptr() if dwu is not None else None,
+                         dwd.data_ptr() if dwd is not None else None)
+    need = backward_workspace_bytes(cfg, T, weight_grads)
+    if need == 0 and T > 0:
+        raise BeamMoeError(BEAM_ERR_CONFIG, "beam_moe_backward_workspace_bytes")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib().beam_moe_backward(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
+                                 _ptr(w_gate), _ptr(w_up), _ptr(w_gate_t), _ptr(w_up_t),
+                                 _ptr(w_down_t), _ptr(dout), ctypes.byref(grads), _ptr(workspace),
+                                 workspace.numel(), _stream(dev, stream))
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_backward")
+    return {"dx": dx, "d_router_w": drw, "d_w_gate": dwg, "d_w_up": dwu, "d_w_down": dwd}
+
+
+def update_bias(expert_bias, expert_counts, gamma, stream=None):
+    """One load-balancing step of the selection bias, in place:
+    b[e] += gamma * sign(mean(counts) - counts[e])."""
+    dev = expert_bias.device
+    _check(expert_bias, "expert_bias", (256,), (torch.float32,), dev)
+    _check(expert_counts, "expert_counts", (256,), (torch.int32,), dev)
+    st = lib().beam_moe_update_bias(_ptr(expert_bias), _ptr(expert_counts), 256, float(gamma),
+                                    _stream(dev, stream))
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_update_bias")
+    return expert_bias
 
 
 def profile_begin(stages=STAGES):

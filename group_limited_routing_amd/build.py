@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libbeam_moe.so")
-SOURCES = ["beam_moe.hip", "router.hip", "permute.hip", "expert_gemm.hip"]
+SOURCES = ["beam_moe.hip", "router.hip", "permute.hip", "expert_gemm.hip", "backward.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

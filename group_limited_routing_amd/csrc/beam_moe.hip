@@ -66,6 +66,45 @@ Layout make_layout(const Shape& s) {
   return L;
 }
 
+// Backward pass: the forward's routing and permutation buffers (its y region
+// holds the input-gradient rows), then the backward's own.
+struct BwdLayout {
+  Layout f;
+  size_t ssel, gu, d, part, dz, pcol, xt, gyt, ht, dgt, dut, total;
+  size_t pstride;  // row length of the transposed copies (columns)
+  int nparts;      // partial sums of h . q per sorted row
+};
+
+BwdLayout make_backward_layout(const Shape& s, bool wgrads) {
+  BwdLayout B{};
+  B.f = make_layout(s);
+  size_t off = B.f.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t P = (size_t)s.T * s.top_k, H = (size_t)s.H, I = (size_t)s.I, E = (size_t)s.E;
+  B.nparts = (int)(I / 256) * 4;
+  B.ssel = take(P * 4);
+  B.gu = take(P * 2 * I * 4);  // fp32: the SwiGLU derivative near its zero needs g exactly
+  B.d = take(P * 2 * I * 2);
+  B.part = take(P * (size_t)B.nparts * 4);
+  B.dz = take(P * 4);
+  B.pcol = take((E + 1) * 4);
+  // every expert's segment is padded to a multiple of 32 columns
+  B.pstride = (P + 32 * E + 31) / 32 * 32;
+  if (wgrads) {
+    B.xt = take(H * B.pstride * 2);
+    B.gyt = take(H * B.pstride * 2);
+    B.ht = take(I * B.pstride * 2);
+    B.dgt = take(I * B.pstride * 2);
+    B.dut = take(I * B.pstride * 2);
+  }
+  B.total = off;
+  return B;
+}
+
 }  // namespace beam
 
 using namespace beam;
@@ -215,18 +254,18 @@ Buffers carve(const Layout& L, void* ws) {
 // fp32 tokens: fp32 MFMA logits straight into z.
 beam_status route_tokens(const Shape& s, const Layout& L, const Buffers& B, const void* x,
                          const float* router_w, const float* bias, float* logits_out,
-                         int32_t* idx, float* w, hipStream_t st) {
+                         int32_t* idx, float* w, hipStream_t st, float* s_sel = nullptr) {
   const int T = s.T;
   if (L.router_ks > 0) {
     STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_x3((const uint16_t*)x, router_w, B.wsplit, B.zpart,
                                                      T, s.H, L.router_ks, st));
     STAGE(BEAM_STAGE_SELECT, launch_select(B.zpart, L.router_ks, (size_t)T * s.E, logits_out, bias, T,
-                                           s.n_group, s.topk_group, s.top_k, idx, w, st));
+                                           s.n_group, s.topk_group, s.top_k, idx, w, s_sel, st));
   } else {
     float* z = logits_out ? logits_out : B.z;
     STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_logits(x, s.x_f32, router_w, z, T, s.H, st));
     STAGE(BEAM_STAGE_SELECT, launch_select(z, 1, 0, nullptr, bias, T, s.n_group, s.topk_group,
-                                           s.top_k, idx, w, st));
+                                           s.top_k, idx, w, s_sel, st));
   }
   return BEAM_OK;
 }
@@ -410,9 +449,184 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
   return BEAM_OK;
 }
 
+beam_status check_backward(const beam_moe_config* cfg) {
+  const beam_status cs = check_config(cfg);
+  if (cs != BEAM_OK) return cs;
+  if (cfg->x_dtype != BEAM_BF16 || cfg->w_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
+  if (cfg->w_layout != BEAM_LAYOUT_PACKED) return BEAM_ERR_CONFIG;
+  if (cfg->hidden % 256 != 0 || cfg->intermediate % 256 != 0) return BEAM_ERR_SHAPE;
+  return BEAM_OK;
+}
+
+beam_status backward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
+                          const float* router_w, const float* expert_bias, const void* w_gate,
+                          const void* w_up, const void* w_gate_t, const void* w_up_t,
+                          const void* w_down_t, const void* dout, const beam_moe_grads* grads,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const beam_status cs = check_backward(cfg);
+  if (cs != BEAM_OK) return cs;
+  if (T < 0 || T > kMaxT) return BEAM_ERR_SHAPE;
+  if (!grads) return BEAM_ERR_NULL;
+  const int nw = (grads->d_w_gate != nullptr) + (grads->d_w_up != nullptr) +
+                 (grads->d_w_down != nullptr);
+  if (nw != 0 && nw != 3) return BEAM_ERR_NULL;
+  const bool wg = nw == 3;
+  if (T == 0) return BEAM_OK;
+  if (!x || !router_w || !expert_bias || !w_gate || !w_up || !w_gate_t || !w_up_t || !w_down_t ||
+      !dout || !grads->dx)
+    return BEAM_ERR_NULL;
+  if (!workspace) return BEAM_ERR_WORKSPACE;
+  if (misaligned(x) || misaligned(router_w) || misaligned(expert_bias) || misaligned(w_gate) ||
+      misaligned(w_up) || misaligned(w_gate_t) || misaligned(w_up_t) || misaligned(w_down_t) ||
+      misaligned(dout) || misaligned(grads->dx) || misaligned(grads->d_router_w) ||
+      misaligned(grads->d_w_gate) || misaligned(grads->d_w_up) || misaligned(grads->d_w_down) ||
+      misaligned(workspace))
+    return BEAM_ERR_ALIGN;
+  const Shape s = shape_of(cfg, T);
+  const BwdLayout BL = make_backward_layout(s, wg);
+  if (workspace_bytes < BL.total) return BEAM_ERR_WORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  const Layout& L = BL.f;
+  Buffers B = carve(L, workspace);
+  const int k = s.top_k, H = s.H, I = s.I;
+  const int BM = wide_bm(s);
+  float* ssel = (float*)(ws + BL.ssel);
+  float* gu = (float*)(ws + BL.gu);
+  uint16_t* dgu = (uint16_t*)(ws + BL.d);
+  float* part = (float*)(ws + BL.part);
+  float* dz = (float*)(ws + BL.dz);
+  int32_t* pcol = (int32_t*)(ws + BL.pcol);
+  uint16_t* dxr = (uint16_t*)(ws + L.y);
+  uint16_t* ht = wg ? (uint16_t*)(ws + BL.ht) : nullptr;
+  uint16_t* dgt = wg ? (uint16_t*)(ws + BL.dgt) : nullptr;
+  uint16_t* dut = wg ? (uint16_t*)(ws + BL.dut) : nullptr;
+  const int cblocks = (int)(BL.pstride / 32);
+
+  const beam_status rs = route_tokens(s, L, B, x, router_w, expert_bias, nullptr, B.idx, B.w, st,
+                                      ssel);
+  if (rs != BEAM_OK) return rs;
+  STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(B.idx, T, k, B.chist, st));
+  STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts, B.offsets,
+                                               B.meta, B.tile_e, B.tile_r, B.e_tstart, B.e_ntiles,
+                                               nullptr, st));
+  STAGE(BEAM_STAGE_PERM_SCATTER, launch_perm_scatter(B.idx, B.w, T, k, s.rsf, B.cbase, B.offsets,
+                                                     B.stok, B.sw, B.inv, st));
+  if (wg) STAGE(BEAM_STAGE_BWD_TRANSPOSE, launch_segment_cols(B.counts, pcol, st));
+
+  GemmArgs g{};
+  g.tile_e = B.tile_e;
+  g.tile_r = B.tile_r;
+  g.e_tstart = B.e_tstart;
+  g.e_ntiles = B.e_ntiles;
+  g.meta = B.meta;
+  g.offsets = B.offsets;
+  g.stok = B.stok;
+  g.max_mtiles = L.max_mtiles;
+  g.pcol = pcol;
+  g.pstride = BL.pstride;
+  // g | u of every sorted row (and h transposed)
+  g.a = x;
+  g.w0 = w_gate;
+  g.w1 = w_up;
+  g.out = gu;
+  g.tout0 = ht;
+  g.K = H;
+  g.N = I;
+  STAGE(BEAM_STAGE_BWD_GATEUP, launch_backward_gemm(2, s, BM, g, st));
+  // q = W_down^T dout[t]; dg | du (and their transposes); partial sums of h . q
+  g.a = dout;
+  g.w0 = w_down_t;
+  g.w1 = nullptr;
+  g.a2 = gu;
+  g.sw = B.sw;
+  g.out = dgu;
+  g.tout0 = dgt;
+  g.tout1 = dut;
+  g.part = part;
+  g.nparts = BL.nparts;
+  STAGE(BEAM_STAGE_BWD_DOWN, launch_backward_gemm(3, s, BM, g, st));
+  // input-gradient rows: W_gate^T dg + W_up^T du
+  g.a = dgu;
+  g.w0 = w_gate_t;
+  g.w1 = w_up_t;
+  g.a2 = nullptr;
+  g.sw = nullptr;
+  g.out = dxr;
+  g.tout0 = g.tout1 = nullptr;
+  g.part = nullptr;
+  g.K = 2 * I;
+  g.N = H;
+  STAGE(BEAM_STAGE_BWD_DX, launch_backward_gemm(4, s, BM, g, st));
+  STAGE(BEAM_STAGE_BWD_TOKEN, launch_token_grad(dxr, B.inv, B.idx, B.w, ssel, part, BL.nparts,
+                                                s.rsf, router_w, T, k, H, dz,
+                                                (uint16_t*)grads->dx, st));
+  if (grads->d_router_w)
+    STAGE(BEAM_STAGE_BWD_ROUTER, launch_router_grad((const uint16_t*)x, H, B.stok, B.offsets, dz,
+                                                    grads->d_router_w, st));
+  if (wg) {
+    uint16_t* xt = (uint16_t*)(ws + BL.xt);
+    uint16_t* gyt = (uint16_t*)(ws + BL.gyt);
+    STAGE(BEAM_STAGE_BWD_TRANSPOSE, launch_gather_t((const uint16_t*)x, H, false, B.stok, B.sw,
+                                                    B.offsets, pcol, xt, BL.pstride, cblocks, st));
+    STAGE(BEAM_STAGE_BWD_TRANSPOSE, launch_gather_t((const uint16_t*)dout, H, true, B.stok, B.sw,
+                                                    B.offsets, pcol, gyt, BL.pstride, cblocks, st));
+    STAGE(BEAM_STAGE_BWD_TRANSPOSE, launch_zero_pads(ht, dgt, dut, I, BL.pstride, B.offsets, pcol,
+                                                     cblocks, st));
+    STAGE(BEAM_STAGE_BWD_WGRAD, launch_wgrad(gyt, ht, H, I, BL.pstride, pcol,
+                                             (uint16_t*)grads->d_w_down, st));
+    STAGE(BEAM_STAGE_BWD_WGRAD, launch_wgrad(dgt, xt, I, H, BL.pstride, pcol,
+                                             (uint16_t*)grads->d_w_gate, st));
+    STAGE(BEAM_STAGE_BWD_WGRAD, launch_wgrad(dut, xt, I, H, BL.pstride, pcol,
+                                             (uint16_t*)grads->d_w_up, st));
+  }
+  return BEAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t beam_moe_backward_workspace_bytes(const beam_moe_config* cfg, int32_t T,
+                                         int32_t with_weight_grads) {
+  if (check_backward(cfg) != BEAM_OK || T < 0 || T > kMaxT) return 0;
+  return make_backward_layout(shape_of(cfg, T), with_weight_grads != 0).total;
+}
+
+beam_status beam_moe_backward(const beam_moe_config* cfg, int32_t T, const void* x,
+                              const float* router_w, const float* expert_bias, const void* w_gate,
+                              const void* w_up, const void* w_gate_t, const void* w_up_t,
+                              const void* w_down_t, const void* dout, const beam_moe_grads* grads,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(cfg, T, x, router_w, expert_bias, w_gate, w_up, w_gate_t, w_up_t, w_down_t,
+                       dout, grads, workspace, workspace_bytes, stream);
+}
+
+beam_status beam_moe_pack_weights_transposed(const void* src, void* dst, int32_t n_experts,
+                                             int32_t rows, int32_t cols, int32_t w_dtype,
+                                             void* stream) {
+  if (!src || !dst) return BEAM_ERR_NULL;
+  if (w_dtype != BEAM_BF16) return BEAM_ERR_DTYPE;
+  if (n_experts < 1 || n_experts > 65535 || rows < 64 || rows % 64 != 0 || cols < 64 ||
+      cols % 64 != 0)
+    return BEAM_ERR_SHAPE;
+  if ((long long)n_experts * rows * cols * 2 > (1LL << 40)) return BEAM_ERR_SHAPE;
+  if (misaligned(src) || misaligned(dst)) return BEAM_ERR_ALIGN;
+  return launch_pack_t(src, dst, n_experts, rows, cols, (hipStream_t)stream) == hipSuccess
+             ? BEAM_OK
+             : BEAM_ERR_HIP;
+}
+
+beam_status beam_moe_update_bias(float* expert_bias, const int32_t* expert_counts,
+                                 int32_t n_experts, float gamma, void* stream) {
+  if (!expert_bias || !expert_counts) return BEAM_ERR_NULL;
+  if (n_experts != kExperts || !isfinite(gamma)) return BEAM_ERR_CONFIG;
+  if (misaligned(expert_bias) || misaligned(expert_counts)) return BEAM_ERR_ALIGN;
+  return launch_bias_step(expert_bias, expert_counts, gamma, (hipStream_t)stream) == hipSuccess
+             ? BEAM_OK
+             : BEAM_ERR_HIP;
+}
 
 beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x,
                              const float* router_w, const float* expert_bias, const void* w_gate,

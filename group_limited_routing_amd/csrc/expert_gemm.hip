@@ -697,7 +697,7 @@ __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const Til
     } else {
       if (valid) {
         // rsf * routing weight of the row (fp8: times the row's activation scale)
-        float rs = p.sw[ti.row0 + row];
+        float rs = p.sw ? p.sw[ti.row0 + row] : 1.f;  // no per-row scale: input gradients
         if constexpr (FP8) rs = p.a_scale[ti.row0 + row] * rs;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
@@ -904,13 +904,31 @@ void gemm_wide_kernel(GemmArgs p) {
 // position g ^ ((r >> 1) & 3) so the 16 rows of a fragment read hit distinct
 // banks; B is 16 row blocks x 1 KB in the packed fragment order.
 
+//
+// Modes: 0 gate/up (A = x rows through the sorted token list, B = the gate and
+// up matrices side by side, out = h); 1 down (A = h rows, out = rsf * w * y).
+// The backward pass adds: 2 gate/up again, storing the pre-activations g | u
+// in fp32 (and h transposed for the weight gradients); 3 the gradient through the
+// down projection and SwiGLU (A = dout rows through the sorted token list,
+// B = W_down transposed, out = dg | du); 4 the input gradient of every row
+// (A = dg | du rows, B = W_gate transposed for the first half of k and W_up
+// transposed for the second, out = dx rows).
+constexpr bool mode_paired(int m) { return m == 0 || m == 2; }
+constexpr bool mode_gathered(int m) { return m == 0 || m == 2 || m == 3; }
+
+template <int MODE, int FM, int FN>
+__device__ __forceinline__ void backward_epilogue(const GemmArgs& p, const TileInfo& ti,
+                                                  const f32x4 (&acc)[FM][FN], int row_base,
+                                                  int n0, int nt, int wn, int r, int g);
+
 template <int MODE, int BM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_dma_kernel(GemmArgs p) {
   constexpr int NS = 4;                        // stages in the ring
   constexpr int A_BYTES = BM * 64, B_BYTES = 256 * 64, STAGE = A_BYTES + B_BYTES;
   constexpr int FM = BM / 32, FN = 4;
-  constexpr int COLS = (MODE == 0) ? 128 : 256;
+  constexpr bool PAIRED = mode_paired(MODE);
+  constexpr int COLS = PAIRED ? 128 : 256;
   constexpr int AI = BM / 128;                 // A DMA instructions per wave per stage
   static_assert(AI == 1 || AI == 2, "row groups per wave");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
@@ -946,19 +964,28 @@ void gemm_dma_kernel(GemmArgs p) {
     const int row = (wave * AI + i) * 16 + (lane >> 2);
     const int chunk = (lane & 3) ^ ((row >> 1) & 3);
     const int ar = min(row, ti.rows - 1);
-    const uint16_t* base = (MODE == 0) ? (const uint16_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K
-                                       : (const uint16_t*)p.a + (size_t)(ti.row0 + ar) * K;
+    const uint16_t* base = mode_gathered(MODE)
+                               ? (const uint16_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K
+                               : (const uint16_t*)p.a + (size_t)(ti.row0 + ar) * K;
     asrc[i] = base + chunk * 8;
   }
-  // B DMA sources: instruction i fills row block wave * 2 + i (MODE 0: 0..7 gate, 8..15 up).
+  // B DMA sources: instruction i fills row block wave * 2 + i (paired modes:
+  // 0..7 gate, 8..15 up). Mode 4 reads w0 for the first half of k and w1 for
+  // the second, each a [N, K / 2] matrix.
+  constexpr bool KSPLIT = MODE == 4;
+  const int KB = KSPLIT ? K / 2 : K;  // reduction length of one weight matrix
   const uint16_t* bsrc[2];
+  const uint16_t* bsrc2[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int rbk = wave * 2 + i;
-    const uint16_t* W = (const uint16_t*)((MODE == 0 && rbk >= 8) ? p.w1 : p.w0);
-    const int blk = (MODE == 0) ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
-    bsrc[i] = W + (size_t)ti.e * N * K + (size_t)blk * 16 * K + lane * 8;
+    const uint16_t* W = (const uint16_t*)((PAIRED && rbk >= 8) ? p.w1 : p.w0);
+    const int blk = PAIRED ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
+    const size_t off = (size_t)ti.e * N * KB + (size_t)blk * 16 * KB + lane * 8;
+    bsrc[i] = W + off;
+    bsrc2[i] = KSPLIT ? (const uint16_t*)p.w1 + off : nullptr;
   }
+  const int kh = KB / 32;  // k-steps per weight matrix
   // DMA of k-step kt into ring slot kt % NS: this wave's first AL row groups
   // of A (the others lie past the expert's last row and are not loaded) and
   // its two weight row blocks.
@@ -969,8 +996,11 @@ void gemm_dma_kernel(GemmArgs p) {
     for (int i = 0; i < AL; ++i)
       dma16(asrc[i] + (size_t)kt * 32, st + (wave * AI + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16(bsrc[i] + (size_t)kt * 512, st + A_BYTES + (wave * 2 + i) * 1024);
+    for (int i = 0; i < 2; ++i) {
+      const uint16_t* bp = (!KSPLIT || kt < kh) ? bsrc[i] + (size_t)kt * 512
+                                                : bsrc2[i] + (size_t)(kt - kh) * 512;
+      dma16(bp, st + A_BYTES + (wave * 2 + i) * 1024);
+    }
   };
 
   int aoff[FM], boff[FN];
@@ -981,7 +1011,7 @@ void gemm_dma_kernel(GemmArgs p) {
   }
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
-    const int rbl = (MODE == 0) ? ((f < 2) ? wn * 2 + f : 8 + wn * 2 + (f - 2)) : wn * 4 + f;
+    const int rbl = PAIRED ? ((f < 2) ? wn * 2 + f : 8 + wn * 2 + (f - 2)) : wn * 4 + f;
     boff[f] = A_BYTES + rbl * 1024 + lane * 16;
   }
   f32x4 acc[FM][FN];
@@ -1046,7 +1076,95 @@ void gemm_dma_kernel(GemmArgs p) {
   else
     run(std::integral_constant<int, FM>{});
 
-  transposed_epilogue<MODE, false, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
+  if constexpr (MODE <= 1)
+    transposed_epilogue<MODE, false, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
+  else if constexpr (MODE == 4)
+    transposed_epilogue<1, false, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
+  else
+    backward_epilogue<MODE, FM, FN>(p, ti, acc, wm * (BM / 2), n0, nt, wn, r, g);
+}
+
+// Epilogues of modes 2 and 3 (lane (r, g) of fragment (fm, fn) holds row
+// row_base + 16 fm + r, columns 16 c + 4 g .. + 3 as in transposed_epilogue).
+// Transposed copies (h, dg, du) go to [I, pcols] matrices whose column of
+// sorted row q is p.pcol[e] + q - offsets[e] (each expert's rows a segment).
+__device__ __forceinline__ void store_col4(uint16_t* base, size_t pstride, int n, size_t col,
+                                           const float (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) base[(size_t)(n + i) * pstride + col] = (uint16_t)f32_to_bf16_bits(v[i]);
+}
+
+template <int MODE, int FM, int FN>
+__device__ __forceinline__ void backward_epilogue(const GemmArgs& p, const TileInfo& ti,
+                                                  const f32x4 (&acc)[FM][FN], int row_base,
+                                                  int n0, int nt, int wn, int r, int g) {
+  const int N = p.N;
+  const size_t ld = 2 * (size_t)N;  // row length of the g | u (fp32) and dg | du (bf16) matrices
+  uint16_t* out = (uint16_t*)p.out;
+  const bool tr = p.tout0 != nullptr;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int row = row_base + fm * 16 + r;
+    const bool valid = row < ti.rows;
+    const size_t grow = (size_t)(ti.row0 + (valid ? row : 0));
+    const size_t col = tr ? (size_t)(p.pcol[ti.e] + (int)grow - p.offsets[ti.e]) : 0;
+    if constexpr (MODE == 2) {
+      constexpr int NF = FN / 2;
+      if (valid) {
+#pragma unroll
+        for (int fn = 0; fn < NF; ++fn) {
+          const int n = n0 + (wn * NF + fn) * 16 + 4 * g;
+          const f32x4 gv = acc[fm][fn], uv = acc[fm][fn + NF];
+          float* gu = (float*)p.out + grow * ld;
+          st16(gu + n, __builtin_bit_cast(u32x4, gv));
+          st16(gu + N + n, __builtin_bit_cast(u32x4, uv));
+          if (tr) {
+            float h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = silu_f32(gv[i]) * uv[i];
+            store_col4((uint16_t*)p.tout0, p.pstride, n, col, h);
+          }
+        }
+      }
+    } else {
+      // dh = rsf * w * q; du = dh * silu(g); dg = dh * u * silu'(g); the row's
+      // share of sum_n h q for the routing-weight gradient
+      const float sw = valid ? p.sw[grow] : 0.f;
+      const float* gu = (const float*)p.a2 + grow * ld;
+      float hq = 0.f;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int n = n0 + (wn * FN + fn) * 16 + 4 * g;
+        if (valid) {
+          const f32x4 gg = __builtin_bit_cast(f32x4, ld16(gu + n));
+          const f32x4 uu = __builtin_bit_cast(f32x4, ld16(gu + N + n));
+          float dg[4], du[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float q = acc[fm][fn][i];
+            const float sg = sigmoid_f32(gg[i]);
+            const float a = gg[i] * sg;
+            const float dh = sw * q;
+            du[i] = dh * a;
+            dg[i] = dh * uu[i] * (sg * (1.f + gg[i] * (1.f - sg)));
+            hq += a * uu[i] * q;
+          }
+          *reinterpret_cast<u32x2*>(out + grow * ld + n) =
+              u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+          *reinterpret_cast<u32x2*>(out + grow * ld + N + n) =
+              u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          if (tr) {
+            store_col4((uint16_t*)p.tout0, p.pstride, n, col, dg);
+            store_col4((uint16_t*)p.tout1, p.pstride, n, col, du);
+          }
+        }
+      }
+      // the 4 lanes of a row (g = 0..3) hold its other columns of this wave
+      hq += __shfl_xor(hq, 16);
+      hq += __shfl_xor(hq, 32);
+      if (valid && g == 0) p.part[grow * p.nparts + nt * 4 + wn] = hq;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- fp8 DMA variant
@@ -1525,6 +1643,29 @@ hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st) {
     launch_variant<0, float, false>(s, g, st);
   else
     launch_variant<0, uint16_t, false>(s, g, st);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static void launch_backward_bm(const Shape& s, int BM, const GemmArgs& g, hipStream_t st) {
+  long long n = (long long)mtile_bound(s, BM) * (g.N / (mode_paired(MODE) ? 128 : 256));
+  n = (n + 7) & ~7LL;
+  if (BM == 256)
+    gemm_dma_kernel<MODE, 256><<<(unsigned)n, 512, 0, st>>>(g);
+  else
+    gemm_dma_kernel<MODE, 128><<<(unsigned)n, 512, 0, st>>>(g);
+}
+
+hipError_t launch_backward_gemm(int mode, const Shape& s, int BM, const GemmArgs& g,
+                                hipStream_t st) {
+  if (mode == 2)
+    launch_backward_bm<2>(s, BM, g, st);
+  else if (mode == 3)
+    launch_backward_bm<3>(s, BM, g, st);
+  else if (mode == 4)
+    launch_backward_bm<4>(s, BM, g, st);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

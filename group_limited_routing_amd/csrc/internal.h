@@ -42,9 +42,10 @@ hipError_t launch_router_logits(const void* x, int x_f32, const float* W, float*
 int router_ksplit(int T, int H);
 hipError_t launch_router_x3(const uint16_t* x, const float* W, uint16_t* wsplit, float* zp, int T,
                             int H, int ks, hipStream_t st);
+// s_sel (nullable): [T, top_k] sigmoid scores of the chosen experts
 hipError_t launch_select(const float* z, int nparts, size_t pstride, float* zout, const float* bias,
                          int T, int n_group, int topk_group, int top_k, int32_t* idx, float* w,
-                         hipStream_t st);
+                         float* s_sel, hipStream_t st);
 hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int32_t* chist, hipStream_t st);
 hipError_t launch_perm_scan(const int32_t* chist, int nchunks, int BM, int32_t* cbase,
                             int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,
@@ -73,9 +74,21 @@ struct GemmArgs {
   uint32_t* hamax;          // fp8 gate/up: per-row running max |h| (float bits)
   int K, N;                 // reduction length and output width
   int max_mtiles;
+  // backward pass only
+  const void* a2;           // g | u rows of the recomputed gate/up pass
+  void* tout0;              // transposed outputs [N, pcols] (null: none)
+  void* tout1;
+  const int32_t* pcol;      // first column of each expert's segment in them
+  size_t pstride;           // their row length (pcols)
+  float* part;              // per-row partial sums of h . q, nparts per row
+  int nparts;
 };
 
 hipError_t launch_gateup(const Shape& s, const GemmArgs& g, hipStream_t st);
+// Backward-pass GEMMs (bf16 tokens, packed bf16 weights; modes 2-4 of the DMA
+// variant) with M-tiles of BM rows; the grid covers mtile_bound(s, BM) tiles.
+hipError_t launch_backward_gemm(int mode, const Shape& s, int BM, const GemmArgs& g,
+                                hipStream_t st);
 hipError_t launch_down(const Shape& s, const GemmArgs& g, hipStream_t st);
 hipError_t launch_pack(const void* src, void* dst, int E, int rows, int cols, int fp8,
                        hipStream_t st);
@@ -92,6 +105,24 @@ constexpr int kResidualMaxH = 16384;
 hipError_t launch_combine_residual(const void* y, const int32_t* inv, int T, int k, int H,
                                    int x_f32, const void* stream_in, const float* gain, float eps,
                                    float keep, float add, void* stream_out, hipStream_t st);
+// backward pass (backward.hip)
+hipError_t launch_segment_cols(const int32_t* counts, int32_t* pcol, hipStream_t st);
+hipError_t launch_gather_t(const uint16_t* src, int H, bool scaled, const int32_t* stok,
+                           const float* sw, const int32_t* offsets, const int32_t* pcol,
+                           uint16_t* out, size_t pstride, int max_blocks, hipStream_t st);
+hipError_t launch_zero_pads(uint16_t* a, uint16_t* b, uint16_t* c, int N, size_t pstride,
+                            const int32_t* offsets, const int32_t* pcol, int max_blocks,
+                            hipStream_t st);
+hipError_t launch_token_grad(const uint16_t* dxr, const int32_t* inv, const int32_t* idx,
+                             const float* w, const float* s_sel, const float* part, int nparts,
+                             float rsf, const float* router_w, int T, int k, int H,
+                             float* dz_sorted, uint16_t* dx, hipStream_t st);
+hipError_t launch_router_grad(const uint16_t* x, int H, const int32_t* stok,
+                              const int32_t* offsets, const float* dz, float* drw, hipStream_t st);
+hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, int M, int N, size_t pstride,
+                        const int32_t* pcol, uint16_t* C, hipStream_t st);
+hipError_t launch_pack_t(const void* src, void* dst, int E, int rows, int cols, hipStream_t st);
+hipError_t launch_bias_step(float* bias, const int32_t* counts, float gamma, hipStream_t st);
 hipError_t launch_quant_x(const void* x, int x_f32, int T, int H, int k, uint8_t* xq, float* xs,
                           uint32_t* hamax, hipStream_t st);
 hipError_t launch_quant_h(const float* hf, const uint32_t* hamax, int rows, int I, uint8_t* hq,

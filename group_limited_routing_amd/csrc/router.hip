@@ -277,7 +277,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ z
                                                      const float* __restrict__ bias, int T,
                                                      int n_group, int topk_group, int top_k,
                                                      int32_t* __restrict__ idx,
-                                                     float* __restrict__ wout) {
+                                                     float* __restrict__ wout,
+                                                     float* __restrict__ sout) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -354,6 +355,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ z
   if (lane < top_k) {
     idx[(size_t)t * top_k + lane] = my_i;
     wout[(size_t)t * top_k + lane] = my_s / sum;
+    if (sout) sout[(size_t)t * top_k + lane] = my_s;
   }
 }
 
@@ -398,9 +400,9 @@ hipError_t launch_router_x3(const uint16_t* x, const float* W, uint16_t* wsplit,
 
 hipError_t launch_select(const float* z, int nparts, size_t pstride, float* zout, const float* bias,
                          int T, int n_group, int topk_group, int top_k, int32_t* idx, float* w,
-                         hipStream_t st) {
+                         float* s_sel, hipStream_t st) {
   select_kernel<<<(T + 3) / 4, 256, 0, st>>>(z, nparts, pstride, zout, bias, T, n_group,
-                                             topk_group, top_k, idx, w);
+                                             topk_group, top_k, idx, w, s_sel);
   return hipGetLastError();
 }
 

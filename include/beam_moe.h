@@ -242,13 +242,94 @@ beam_status beam_moe_forward_residual(const beam_moe_config* cfg, int32_t T, con
 beam_status beam_moe_pack_weights(const void* src, void* dst, int32_t n_experts, int32_t rows,
                                   int32_t cols, int32_t w_dtype, void* stream);
 
+/*
+ * The backward pass of the block, for training and adapter fine-tuning
+ * (launch post "Introducing Beam", section "Post-training Beam": GRPO with
+ * full recomputation and bf16 gradients; rank-16 adapters on the expert
+ * layers). It recomputes the routing and the gate/up pass from x, then
+ * applies the chain rule to L = sum(dout * out):
+ *   slot j of token t, expert e, sorted row q, g = W_gate[e] x, u = W_up[e] x,
+ *   h = silu(g) u, y = W_down[e] h, w the normalised weight, s the chosen
+ *   sigmoid scores with sum S:
+ *   dh = rsf w (W_down[e]^T dout[t]);  du = dh silu(g);  dg = dh u silu'(g)
+ *   dx[t] = sum_j (W_gate[e]^T dg + W_up[e]^T du) + sum_j dz_j W_r[e_j]
+ *   dw_j = rsf <dout[t], y>;  ds_j = (dw_j - sum_i w_i dw_i) / S;
+ *   dz_j = ds_j s_j (1 - s_j);  d W_r[e] = sum over e's slots of dz x[t]
+ *   d W_down[e] = sum (rsf w dout[t]) h^T;  d W_gate[e] = sum dg x[t]^T;
+ *   d W_up[e] = sum du x[t]^T
+ * The expert choice is piecewise constant: the selection bias gets no
+ * gradient (it moves by beam_moe_update_bias instead).
+ *
+ * Scope: x_dtype BEAM_BF16; w_dtype BEAM_BF16 in BEAM_LAYOUT_PACKED; hidden
+ * and intermediate multiples of 256 (else BEAM_ERR_DTYPE / BEAM_ERR_CONFIG /
+ * BEAM_ERR_SHAPE).
+ *   x [T, H] bf16, router_w [E, H] fp32, expert_bias [E] fp32: as for forward.
+ *   w_gate, w_up: packed, as for forward (the gate/up recomputation).
+ *   w_gate_t, w_up_t: beam_moe_pack_weights_transposed of w_gate / w_up
+ *     (packed [E, H, I]); w_down_t: of w_down (packed [E, I, H]).
+ *   dout [T, H] bf16: gradient of the block output.
+ * Outputs (beam_moe_grads; all device memory, overwritten):
+ *   dx [T, H] bf16 (required).
+ *   d_router_w [E, H] fp32, or NULL to skip.
+ *   d_w_gate, d_w_up [E, I, H] bf16 and d_w_down [E, H, I] bf16 (row-major,
+ *     the forward's storage order): all three or none (NULL). Experts no
+ *     token chose get zeros.
+ * Workspace: beam_moe_backward_workspace_bytes(cfg, T, with_weight_grads).
+ * Deterministic (no floating-point atomics). Errors as for the forward;
+ * BEAM_ERR_NULL if grads or grads->dx is NULL or only some of the three
+ * weight-gradient pointers are set.
+ */
+typedef struct beam_moe_grads {
+  void* dx;
+  float* d_router_w;
+  void* d_w_gate;
+  void* d_w_up;
+  void* d_w_down;
+} beam_moe_grads;
+
+size_t beam_moe_backward_workspace_bytes(const beam_moe_config* cfg, int32_t T,
+                                         int32_t with_weight_grads);
+
+beam_status beam_moe_backward(const beam_moe_config* cfg, int32_t T, const void* x,
+                              const float* router_w, const float* expert_bias, const void* w_gate,
+                              const void* w_up, const void* w_gate_t, const void* w_up_t,
+                              const void* w_down_t, const void* dout, const beam_moe_grads* grads,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The packed layout of each matrix's transpose: n_experts row-major
+ * [rows, cols] bf16 matrices at `src` become the packed (BEAM_LAYOUT_PACKED)
+ * form of [cols, rows] at `dst` (same size; the reduction runs along the
+ * source rows). Used for the backward pass's products with W^T. rows and
+ * cols multiples of 64; w_dtype BEAM_BF16 only. Errors: BEAM_ERR_NULL,
+ * BEAM_ERR_SHAPE, BEAM_ERR_DTYPE, BEAM_ERR_ALIGN, BEAM_ERR_HIP.
+ */
+beam_status beam_moe_pack_weights_transposed(const void* src, void* dst, int32_t n_experts,
+                                             int32_t rows, int32_t cols, int32_t w_dtype,
+                                             void* stream);
+
+/*
+ * One load-balancing step of the selection bias (transformers model doc
+ * "Beam", "Overview": a learned per-expert bias balances the load in place
+ * of an auxiliary loss; the launch post names DeepSeek-V3's routing scheme,
+ * whose balancing rule this is): for every expert,
+ *   expert_bias[e] += gamma * sign(mean load - expert_counts[e]),
+ * the sign taken exactly (integer comparison), the addition in fp32.
+ * expert_bias [256] fp32 (in place), expert_counts [256] int32 (e.g. from
+ * beam_moe_forward). Errors: BEAM_ERR_NULL, BEAM_ERR_CONFIG (n_experts not
+ * 256 or gamma not finite), BEAM_ERR_ALIGN, BEAM_ERR_HIP.
+ */
+beam_status beam_moe_update_bias(float* expert_bias, const int32_t* expert_counts,
+                                 int32_t n_experts, float gamma, void* stream);
+
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* beam_moe_status_string(int32_t status);
 
 /*
  * Stage timing. The kernels of one call, in launch order (forward: all that
  * apply to its dtypes; route: the first two, plus the histogram and scan when
- * counts are requested).
+ * counts are requested; backward: the routing and permutation stages, then
+ * the BEAM_STAGE_BWD_ ones).
  */
 typedef enum beam_stage {
   BEAM_STAGE_ROUTER_LOGITS = 0, /* fp32 router logits */
@@ -261,11 +342,19 @@ typedef enum beam_stage {
   BEAM_STAGE_QUANT_H = 7,       /* fp8 weights only: per-row E4M3 quantisation of h */
   BEAM_STAGE_DOWN = 8,          /* grouped down GEMM, scaled by rsf * weight */
   BEAM_STAGE_COMBINE = 9,       /* weighted combine into the output */
-  BEAM_STAGE_COUNT = 10
+  /* backward pass */
+  BEAM_STAGE_BWD_GATEUP = 10,   /* gate/up recomputation: g | u (and h transposed) */
+  BEAM_STAGE_BWD_DOWN = 11,     /* W_down^T dout, SwiGLU backward: dg | du */
+  BEAM_STAGE_BWD_DX = 12,       /* W_gate^T dg + W_up^T du per row */
+  BEAM_STAGE_BWD_TOKEN = 13,    /* routing-weight gradient, dz, dx per token */
+  BEAM_STAGE_BWD_ROUTER = 14,   /* router-weight gradient */
+  BEAM_STAGE_BWD_TRANSPOSE = 15,/* transposed operand copies for the weight gradients */
+  BEAM_STAGE_BWD_WGRAD = 16,    /* weight-gradient GEMMs */
+  BEAM_STAGE_COUNT = 17
 } beam_stage;
 
 /*
- * beam_moe_profile_begin(mask): from now on, every route/forward call in the
+ * beam_moe_profile_begin(mask): from now on, every route/forward/backward call in the
  * process records a pair of HIP timing events around the launch of each
  * stage s with bit (1 << s) set in `mask`, on the call's stream. Clears
  * earlier records. The library creates the events (no device memory).

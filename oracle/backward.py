@@ -48,7 +48,7 @@ def dsilu(g):
 
 
 def backward(x, router_w, expert_bias, experts, dout, n_group=8, topk_group=4, top_k=8,
-             routed_scaling_factor=2.5, routing=None, weight_grads=True):
+             routed_scaling_factor=2.5, routing=None, weight_grads=True, only_experts=None):
     """Gradients of L = sum(dout * out) for the block's forward.
 
     ``experts`` as for :func:`oracle.experts.forward` (three arrays or a
@@ -62,6 +62,10 @@ def backward(x, router_w, expert_bias, experts, dout, n_group=8, topk_group=4, t
     * ``dw`` [T, top_k] (gradient of the normalised weights), ``ds`` and
       ``dz`` [T, top_k] (of the chosen scores and logits);
     * ``route``: the routing dict of :func:`oracle.routing.route`.
+
+    ``only_experts`` (a set of expert indices) runs only those experts: their
+    weight gradients are complete (they depend on no other expert), while
+    dx, dw and the router gradient then lack the other experts' terms.
     """
     x = np.asarray(x, dtype=np.float64)
     W_r = np.asarray(router_w, dtype=np.float64)
@@ -80,6 +84,8 @@ def backward(x, router_w, expert_bias, experts, dout, n_group=8, topk_group=4, t
     dw = np.zeros(idx.shape)
     grads = {"d_w_gate": {}, "d_w_up": {}, "d_w_down": {}}
     for e in np.unique(idx):
+        if only_experts is not None and int(e) not in only_experts:
+            continue
         tok, slot = np.nonzero(idx == e)
         wg, wu, wd = (np.asarray(m, dtype=np.float64) for m in get(int(e)))
         xr = x[tok]

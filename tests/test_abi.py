@@ -166,6 +166,55 @@ def test_residual_checks(L):
                     ws=None) == gl.BEAM_OK
 
 
+def _bwd(L, cfg, T, grads, **over):
+    p = dict(x=FAKE, rw=FAKE, b=FAKE, wg=FAKE, wu=FAKE, wgt=FAKE, wut=FAKE, wdt=FAKE, dout=FAKE,
+             ws=FAKE)
+    p.update(over)
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.beam_moe_backward(ctypes.byref(cfg), T, v(p["x"]), v(p["rw"]), v(p["b"]), v(p["wg"]),
+                               v(p["wu"]), v(p["wgt"]), v(p["wut"]), v(p["wdt"]), v(p["dout"]),
+                               None if grads is None else ctypes.byref(grads), v(p["ws"]),
+                               1 << 40, None)
+
+
+def test_backward_checks(L):
+    """Backward: bf16 tokens and packed bf16 weights only, hidden and
+    intermediate multiples of 256, dx required, weight gradients all or none."""
+    c = beam_cfg(w_layout=gl.BEAM_LAYOUT_PACKED)
+    G = lambda **kw: gl.BeamMoeGrads(**dict(dict(dx=FAKE, d_router_w=FAKE), **kw))
+    assert _bwd(L, beam_cfg(), 8, G()) == gl.BEAM_ERR_CONFIG                       # row-major
+    assert _bwd(L, beam_cfg(w_layout=1, x_dtype=gl.BEAM_F32), 8, G()) == gl.BEAM_ERR_DTYPE
+    assert _bwd(L, beam_cfg(w_layout=1, w_dtype=gl.BEAM_FP8_E4M3), 8, G()) == gl.BEAM_ERR_DTYPE
+    assert _bwd(L, beam_cfg(w_layout=1, hidden=5120 + 128), 8, G()) == gl.BEAM_ERR_SHAPE
+    assert _bwd(L, beam_cfg(w_layout=1, intermediate=2560 - 128), 8, G()) == gl.BEAM_ERR_SHAPE
+    assert _bwd(L, c, 8, None) == gl.BEAM_ERR_NULL
+    assert _bwd(L, c, 8, G(dx=None)) == gl.BEAM_ERR_NULL
+    assert _bwd(L, c, 8, G(d_w_gate=FAKE, d_w_up=FAKE)) == gl.BEAM_ERR_NULL      # two of three
+    for name in ["x", "rw", "b", "wg", "wu", "wgt", "wut", "wdt", "dout"]:
+        assert _bwd(L, c, 8, G(), **{name: None}) == gl.BEAM_ERR_NULL, name
+        assert _bwd(L, c, 8, G(), **{name: FAKE + 4}) == gl.BEAM_ERR_ALIGN, name
+    assert _bwd(L, c, 8, G(d_router_w=FAKE + 4)) == gl.BEAM_ERR_ALIGN
+    assert _bwd(L, c, 8, G(), ws=None) == gl.BEAM_ERR_WORKSPACE
+    assert _bwd(L, c, 0, G(), x=None, ws=None) == gl.BEAM_OK
+    assert _bwd(L, c, -1, G()) == gl.BEAM_ERR_SHAPE
+    # workspace: more with the weight gradients' transposed operands; 0 outside the scope
+    a = gl.backward_workspace_bytes(c, 4096, False)
+    b = gl.backward_workspace_bytes(c, 4096, True)
+    assert 0 < a < b
+    assert gl.backward_workspace_bytes(beam_cfg(), 4096, False) == 0
+    v = ctypes.c_void_p
+    pt = L.beam_moe_pack_weights_transposed
+    assert pt(v(FAKE), v(FAKE), 256, 2560, 5120, gl.BEAM_FP8_E4M3, None) == gl.BEAM_ERR_DTYPE
+    assert pt(v(FAKE), v(FAKE), 256, 2560 + 32, 5120, gl.BEAM_BF16, None) == gl.BEAM_ERR_SHAPE
+    assert pt(None, v(FAKE), 256, 2560, 5120, gl.BEAM_BF16, None) == gl.BEAM_ERR_NULL
+    assert pt(v(FAKE), v(FAKE + 8), 256, 2560, 5120, gl.BEAM_BF16, None) == gl.BEAM_ERR_ALIGN
+    ub = L.beam_moe_update_bias
+    assert ub(None, v(FAKE), 256, 1e-3, None) == gl.BEAM_ERR_NULL
+    assert ub(v(FAKE), v(FAKE), 128, 1e-3, None) == gl.BEAM_ERR_CONFIG
+    assert ub(v(FAKE), v(FAKE), 256, float("nan"), None) == gl.BEAM_ERR_CONFIG
+    assert ub(v(FAKE + 4), v(FAKE), 256, 1e-3, None) == gl.BEAM_ERR_ALIGN
+
+
 def test_workspace_size(L):
     c = beam_cfg()
     need = gl.workspace_bytes(c, 64)
@@ -212,6 +261,9 @@ def test_library_links_every_kernel(L):
     for kernel in ["gemm_dma4_kernel", "router_logits_kernel", "router_split_kernel", "router_x3_kernel", "select_kernel", "perm_hist_kernel", "perm_scan_kernel",
                    "perm_scatter_kernel", "gemm_stream_kernel", "gemm_tiled_kernel",
                    "gemm_wide_kernel", "gemm_dma_kernel", "gemm_dma8_kernel", "gemm_stream4_kernel",
-                   "combine_kernel", "combine_residual_kernel", "pack_mx_scales_kernel", "quant_x_kernel",
+                   "combine_kernel", "combine_residual_kernel", "pack_mx_scales_kernel",
+                   "segment_cols_kernel", "gather_t_kernel", "zero_pads_kernel",
+                   "token_grad_kernel", "router_grad_kernel", "gemm_wgrad_kernel",
+                   "pack_t_kernel", "bias_step_kernel", "quant_x_kernel",
                    "quant_h_kernel", "pack_kernel"]:
         assert f"__device_stub__{kernel}" in syms, kernel

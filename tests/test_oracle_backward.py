@@ -152,3 +152,16 @@ def test_dsilu_closed_form():
     fd = (oracle.experts.silu(g + h) - oracle.experts.silu(g - h)) / (2 * h)
     np.testing.assert_allclose(ob.dsilu(g), fd, rtol=1e-7, atol=1e-9)
     assert ob.dsilu(0.0) == 0.5
+
+
+def test_only_experts_keeps_their_weight_gradients():
+    x, rw, b, wg, wu, wd, dout = _problem(24, 16, 8, 32, 6, scale=2.0)
+    kw = dict(n_group=8, topk_group=4, top_k=8)
+    full = ob.backward(x, rw, b, (wg, wu, wd), dout, **kw)
+    chosen = sorted(full["d_w_gate"])
+    sub = set(chosen[::3])
+    part = ob.backward(x, rw, b, (wg, wu, wd), dout, only_experts=sub, **kw)
+    assert set(part["d_w_gate"]) == sub
+    for name in ("d_w_gate", "d_w_up", "d_w_down"):
+        for e in sub:
+            np.testing.assert_array_equal(part[name][e], full[name][e])

@@ -234,6 +234,98 @@ class Bench:
         return {"ms_per_step": ms_step, "wall_s": wall, "gateup_ms": gu_ms / gu_n, "stages_ms": stages}
 
 
+def backward_work(cfg, active):
+    """Bytes each backward stage moves by design (weights of the active
+    experts, its input and output tensors) and its flops."""
+    T, H, I, k, E = cfg["T"], cfg["hidden"], cfg["intermediate"], cfg["top_k"], cfg["n_experts"]
+    P = T * k
+    w = active * I * H * 2          # one bf16 matrix of every active expert
+    return {
+        "bwd_gateup": (2 * w + T * H * 2 + P * 2 * I * 4 + P * I * 2, 4.0 * P * H * I),
+        "bwd_down": (w + T * H * 2 + P * 2 * I * 4 + P * 2 * I * 2 + 2 * P * I * 2, 2.0 * P * H * I),
+        "bwd_dx": (2 * w + P * 2 * I * 2 + P * H * 2, 4.0 * P * H * I),
+        "bwd_wgrad": (3 * E * H * I * 2 + 3 * P * H * 2 + 3 * P * I * 2, 6.0 * P * H * I),
+    }
+
+
+class BackwardBench:
+    """The backward pass (gradients of x, the router and the expert weights)
+    on a workload's inputs, with a seeded N(0, 1) output gradient."""
+
+    def __init__(self, cfg, dev, weights, packed=None):
+        import torch
+        import group_limited_routing_amd as gl
+        import workloads
+        self.torch, self.gl, self.cfg = torch, gl, cfg
+        x, rw, b = workloads.make_small_inputs(cfg, 0)
+        self.x, self.rw, self.b = x.to(dev), rw.to(dev), b.to(dev)
+        self.dout = workloads.normal((cfg["T"], cfg["hidden"]), 1.0, 0, "dout").to(torch.bfloat16).to(dev)
+        w = weights
+        fwd = packed if packed is not None else {
+            k: gl.pack_weights(w[k]) for k in ("w_gate", "w_up")}
+        self.pw = {"w_gate": fwd["w_gate"], "w_up": fwd["w_up"],
+                   "w_gate_t": gl.pack_weights_transposed(w["w_gate"]),
+                   "w_up_t": gl.pack_weights_transposed(w["w_up"]),
+                   "w_down_t": gl.pack_weights_transposed(w["w_down"])}
+        c = gl.make_config(cfg["hidden"], cfg["intermediate"], cfg["n_experts"], cfg["n_group"],
+                           cfg["topk_group"], cfg["top_k"], cfg["routed_scaling_factor"],
+                           torch.bfloat16, torch.bfloat16, packed=True)
+        self.ws = torch.empty(gl.backward_workspace_bytes(c, cfg["T"], True), dtype=torch.uint8,
+                              device=dev)
+        r = gl.route(self.x, self.rw, self.b, n_group=cfg["n_group"], topk_group=cfg["topk_group"],
+                     top_k=cfg["top_k"], return_counts=True)
+        self.active = int((r["expert_counts"].cpu() > 0).sum())
+
+    def step(self):
+        p = self.pw
+        return self.gl.backward(self.x, self.rw, self.b, p["w_gate"], p["w_up"], p["w_gate_t"],
+                                p["w_up_t"], p["w_down_t"], self.dout, weight_grads=True,
+                                n_group=self.cfg["n_group"], topk_group=self.cfg["topk_group"],
+                                top_k=self.cfg["top_k"],
+                                routed_scaling_factor=self.cfg["routed_scaling_factor"],
+                                workspace=self.ws)
+
+    def run(self, steps, warmup):
+        torch, gl = self.torch, self.gl
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            self.step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gl.profile_begin()
+        for _ in range(min(steps, 5)):
+            self.step()
+        torch.cuda.synchronize()
+        prof = gl.profile_end()
+        per_step = {k: round(v[0] / min(steps, 5), 4) for k, v in prof.items()}
+        return ms, per_step
+
+
+def backward_line(cfg, dev, weights, steps, packed=None):
+    bb = BackwardBench(cfg, dev, weights, packed)
+    ms, per_step = bb.run(steps, 2)
+    work = backward_work(cfg, bb.active)
+    # roofline of the longest stage (its launches in one step)
+    name = max(work, key=lambda k: per_step.get(k, 0.0))
+    by, fl = work[name]
+    rl = roofline(by, fl, per_step[name] / 1e3, "bf16")
+    out = {"workload": f"backward of {describe(cfg)}; gradients of x, the router and all "
+                       "expert weights (bf16), output gradient N(0, 1)",
+           "value": round(cfg["T"] / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+           "steps": steps, "active_experts": bb.active,
+           "roofline": dict(rl, stage=name, launch_ms=per_step[name], algorithmic_bytes=by,
+                            algorithmic_flops=fl),
+           "stages_ms_per_step": per_step}
+    del bb
+    return out
+
+
 def cpu_baseline(cfg, bench, n_tokens):
     """The oracle on the first n_tokens tokens of the same inputs (float64)."""
     import numpy as np
@@ -364,6 +456,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-residual", action="store_true",
                     help="skip timing the block with its fused residual step")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward pass at the prefill shape")
+    ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens the oracle runs on (default: 64, MXFP4 weights 4; ~10-30 s)")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -455,6 +550,10 @@ def main():
                       "stages_ms": pres["stages_ms"]},
         }
         del pb
+    if args.workload == "decode" and not args.no_backward:
+        line["backward"] = backward_line(workloads.workload("prefill"), dev, bench.w,
+                                         args.backward_steps, bench.pw)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         n_cpu = args.cpu_tokens or (4 if cfg["w_dtype"] == "mxfp4" else 64)
         line["cpu_baseline"] = cpu_baseline(cfg, bench, min(n_cpu, cfg["T"]))

@@ -241,69 +241,84 @@ hipError_t launch_router_grad(const uint16_t* x, int H, const int32_t* stok,
 // C[e] (M x N, bf16, row-major) = A_e B_e^T, where A_e and B_e are expert e's
 // segments of the transposed copies A [M, pcols] and B [N, pcols] (the
 // reduction runs over the expert's sorted rows; pad columns are zero). An
-// expert with no rows gets a zero matrix. 256 x 256 tiles, 8 waves as a 2 x 4
-// grid of 128 x 64, operands by DMA into a 4-stage LDS ring of 32-column
-// steps (both operands stored like the A tile of the DMA variant: row r's
-// 16-byte chunk g at position g ^ ((r >> 1) & 3)).
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// expert with no rows gets a zero matrix. TM x TN tiles, WAVES waves as a
+// 2 x (WAVES / 2) grid, operands by DMA into an NS-stage LDS ring of
+// 32-column steps (both operands stored like the A tile of the DMA variant:
+// row r's 16-byte chunk g at position g ^ ((r >> 1) & 3)).
+template <int TM, int TN, int WAVES, int NS>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void gemm_wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm, int M,
                        int N, size_t pstride, const int32_t* __restrict__ pcol,
                        uint16_t* __restrict__ C) {
-  constexpr int NS = 4, TB = 256 * 64, STAGE = 2 * TB;
-  constexpr int FM = 8, FN = 4, PER = 4;
+  constexpr int WN = WAVES / 2;                    // waves along N
+  constexpr int WTM = TM / 2, WTN = TN / WN;       // wave tile
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int TA = TM * 64, STAGE = (TM + TN) * 64;
+  constexpr int AI = TM / 16 / WAVES, BI = TN / 16 / WAVES;  // DMA instructions per wave
+  constexpr int PER = AI + BI;
+  static_assert(AI >= 1 && BI >= 1 && FM >= 1 && FN >= 1, "tile shape");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
-  const int mtn = M / 256, ntn = N / 256;
-  const int b = blockIdx.x;
-  const int e = b / (mtn * ntn), rem = b % (mtn * ntn);
-  const int m0 = (rem / ntn) * 256, n0 = (rem % ntn) * 256;
+  const int mtn = M / TM, ntn = N / TN;
+  // XCD-contiguous numbering: the blocks on one XCD (b % 8) take a contiguous
+  // range of tiles, so an expert's tiles, which share operand rows, meet in
+  // that XCD's L2. Inside an expert the N-tile runs fastest.
+  const int n_tiles = kExperts * mtn * ntn, b = blockIdx.x;
+  if (b >= n_tiles) return;
+  const int xcd = b & 7, per = n_tiles >> 3, extra = n_tiles & 7;
+  const int j = xcd * per + min(xcd, extra) + (b >> 3);
+  const int e = j / (mtn * ntn), rem = j % (mtn * ntn);
+  const int m0 = (rem / ntn) * TM, n0 = (rem % ntn) * TN;
   const int c0 = pcol[e], nk = (pcol[e + 1] - c0) / 32;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3, r = lane & 15, g = lane >> 4;
-  // DMA sources: instruction i of this wave fills rows 16 (2 wave + i) .. of a tile
-  const uint16_t* asrc[2];
-  const uint16_t* bsrc[2];
+  const int wm = wave / WN, wn = wave % WN, r = lane & 15, g = lane >> 4;
+  // DMA sources: instruction i of this wave fills rows 16 (wave * AI + i) .. of the tile
+  const uint16_t* asrc[AI];
+  const uint16_t* bsrc[BI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = (wave * 2 + i) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
-    asrc[i] = A + (size_t)(m0 + row) * pstride + c0 + chunk * 8;
-    bsrc[i] = Bm + (size_t)(n0 + row) * pstride + c0 + chunk * 8;
+  for (int i = 0; i < AI; ++i) {
+    const int row = (wave * AI + i) * 16 + (lane >> 2);
+    asrc[i] = A + (size_t)(m0 + row) * pstride + c0 + (((lane & 3) ^ ((row >> 1) & 3)) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int row = (wave * BI + i) * 16 + (lane >> 2);
+    bsrc[i] = Bm + (size_t)(n0 + row) * pstride + c0 + (((lane & 3) ^ ((row >> 1) & 3)) * 8);
   }
   auto issue = [&](int kt) {
     uint8_t* st = smem + (kt % NS) * STAGE;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      dma16(asrc[i] + (size_t)kt * 32, st + (wave * 2 + i) * 1024);
-      dma16(bsrc[i] + (size_t)kt * 32, st + TB + (wave * 2 + i) * 1024);
-    }
+    for (int i = 0; i < AI; ++i) dma16(asrc[i] + (size_t)kt * 32, st + (wave * AI + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < BI; ++i) dma16(bsrc[i] + (size_t)kt * 32, st + TA + (wave * BI + i) * 1024);
   };
   int aoff[FM], boff[FN];
 #pragma unroll
   for (int f = 0; f < FM; ++f) {
-    const int row = wm * 128 + f * 16 + r;
+    const int row = wm * WTM + f * 16 + r;
     aoff[f] = row * 64 + ((g ^ ((row >> 1) & 3)) << 4);
   }
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
-    const int row = wn * 64 + f * 16 + r;
-    boff[f] = TB + row * 64 + ((g ^ ((row >> 1) & 3)) << 4);
+    const int row = wn * WTN + f * 16 + r;
+    boff[f] = TA + row * 64 + ((g ^ ((row >> 1) & 3)) << 4);
   }
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < nk) issue(s0);
   for (int kt = 0; kt < nk; ++kt) {
+    // stage kt done for this wave (at most the later issued stages outstanding) ...
     if (kt + NS - 2 < nk)
       wait_vmcnt<(NS - 2) * PER>();
     else
       wait_vmcnt<0>();
-    barrier_only();
+    barrier_only();  // ... and for every wave; all reads of kt - 1 retired
     asm volatile("" ::: "memory");
     if (kt + NS - 1 < nk) issue(kt + NS - 1);
     const uint8_t* st = smem + (kt % NS) * STAGE;
@@ -315,22 +330,23 @@ void gemm_wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = mfma_bf16(as_bf16x8(bfr[j]), as_bf16x8(af[i]), acc[i][j]);
+      for (int jn = 0; jn < FN; ++jn)
+        acc[i][jn] = mfma_bf16(as_bf16x8(bfr[jn]), as_bf16x8(af[i]), acc[i][jn]);
     wait_lgkmcnt0();
     asm volatile("" ::: "memory");
   }
-  // lane (r, g) of fragment (i, j): row m0 + 128 wm + 16 i + r, columns
-  // n0 + 64 wn + 16 j + 4 g .. + 3
+  // lane (r, g) of fragment (i, jn): row m0 + WTM wm + 16 i + r, columns
+  // n0 + WTN wn + 16 jn + 4 g .. + 3
   uint16_t* Ce = C + (size_t)e * M * N;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int row = m0 + wm * 128 + i * 16 + r;
+    const int row = m0 + wm * WTM + i * 16 + r;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * 64 + j * 16 + 4 * g;
+    for (int jn = 0; jn < FN; ++jn) {
+      const int n = n0 + wn * WTN + jn * 16 + 4 * g;
+      const f32x4 v = acc[i][jn];
       *reinterpret_cast<u32x2*>(Ce + (size_t)row * N + n) =
-          u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
   }
 }
@@ -339,7 +355,7 @@ hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, int M, int N, size
                         const int32_t* pcol, uint16_t* C, hipStream_t st) {
   if (M % 256 || N % 256) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)kExperts * (M / 256) * (N / 256);
-  gemm_wgrad_kernel<<<blocks, 512, 0, st>>>(A, B, M, N, pstride, pcol, C);
+  gemm_wgrad_kernel<256, 256, 8, 4><<<blocks, 512, 0, st>>>(A, B, M, N, pstride, pcol, C);
   return hipGetLastError();
 }
 

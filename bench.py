@@ -422,7 +422,7 @@ def write_traffic(fetch_dir, write_dir, workload):
     hbm = (f["kib"] * f["factor"] + w["kib"] * w["factor"]) * 1024
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <dir> -o run --output-format csv "
            f"-- python3 /root/repo/bench.py --workload {workload} --steps 3 --warmup 1 --no-prefill "
-           "--no-cpu-baseline --calibrate-copy")
+           "--no-residual --no-backward --no-cpu-baseline --calibrate-copy")
     path = os.path.join(ROOT, "profiles", f"gateup_{workload}_counters.txt")
     with open(path, "w") as fh:
         fh.write(f"# HBM traffic of the gate/up grouped GEMM, workload {workload}, one MI355X\n")

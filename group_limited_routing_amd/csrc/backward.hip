@@ -46,18 +46,19 @@ __device__ __forceinline__ int segment_of(const int32_t* pcol, int col) {
 }
 
 // ---------------------------------------------------------------- transposed rows
-// out[h][col] = scale(q) * src[stok[q]][h] for the sorted rows q of every
+// out(h, col) = scale(q) * src[stok[q]][h] for the sorted rows q of every
 // expert, col = pcol[e] + q - offsets[e]; the pad columns of each segment are
-// zero. A workgroup moves a 32-column x 64-row block through LDS: reads of
-// 32 source rows (128 B each), writes of 64 output rows (64 B each).
-// SCALED: scale(q) = sw[q] (rsf * routing weight); else 1.
+// zero. out is [H, pcols] in 32-column blocks (element (h, c) at
+// ((c / 32) H + h) 32 + c % 32). A workgroup moves 32 columns x 64 rows
+// through LDS: reads of 32 source rows (128 B each), one contiguous 4 KB
+// write. SCALED: scale(q) = sw[q] (rsf * routing weight); else 1.
 template <bool SCALED>
 __global__ __launch_bounds__(256) void gather_t_kernel(const uint16_t* __restrict__ src, int H,
                                                        const int32_t* __restrict__ stok,
                                                        const float* __restrict__ sw,
                                                        const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ pcol,
-                                                       uint16_t* __restrict__ out, size_t pstride) {
+                                                       uint16_t* __restrict__ out) {
   __shared__ float tile[32][65];
   const int col0 = blockIdx.x * 32, h0 = blockIdx.y * 64;
   const int e = segment_of(pcol, col0);
@@ -88,45 +89,56 @@ __global__ __launch_bounds__(256) void gather_t_kernel(const uint16_t* __restric
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(tile[c8 + 2 * i][hr], tile[c8 + 2 * i + 1][hr]);
-  st16(out + (size_t)(h0 + hr) * pstride + col0 + c8, o);
+  st16(out + (((size_t)(col0 >> 5) * H + h0 + hr) << 5) + c8, o);
 }
 
 // Zero the pad columns (past each expert's rows) of up to three [N, pcols]
-// matrices written by the GEMM epilogues. One thread per (row, column block).
+// matrices in 32-column blocks written by the GEMM epilogues: only each
+// expert's last block has pads, N contiguous 64-byte rows. One workgroup per
+// expert, a thread per 16-byte chunk (chunks holding live columns keep them).
 __global__ __launch_bounds__(256) void zero_pads_kernel(uint16_t* a, uint16_t* b, uint16_t* c,
-                                                        int N, size_t pstride,
-                                                        const int32_t* __restrict__ offsets,
+                                                        int N, const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ pcol) {
-  const int col0 = blockIdx.x * 32;
-  const int e = segment_of(pcol, col0);
-  if (e < 0) return;
-  const int live = offsets[e + 1] - offsets[e] - (col0 - pcol[e]);  // rows of this block
-  if (live >= 32) return;
-  for (int row = threadIdx.x; row < N; row += 256) {
-    const size_t base = (size_t)row * pstride + col0;
-    for (int i = live; i < 32; ++i) {
-      if (a) a[base + i] = 0;
-      if (b) b[base + i] = 0;
-      if (c) c[base + i] = 0;
+  const int e = blockIdx.x;
+  const int n_e = offsets[e + 1] - offsets[e], live = n_e & 31;
+  if (live == 0) return;  // no pads (or no rows at all)
+  const size_t blk = (size_t)((pcol[e] + n_e) >> 5) * N * 32;
+  for (int q = threadIdx.x; q < N * 4; q += 256) {
+    const int c8 = (q & 3) * 8;
+    if (c8 + 8 <= live) continue;
+    const size_t off = blk + (size_t)(q >> 2) * 32 + c8;
+    uint16_t* bufs[3] = {a, b, c};
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      if (!bufs[m]) continue;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (c8 < live) {  // the chunk holds live columns: keep them
+        const u32x4 old = ld16(bufs[m] + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = c8 + 2 * i;
+          v[i] = (col + 1 < live) ? old[i] : (col < live ? (old[i] & 0xffffu) : 0u);
+        }
+      }
+      st16(bufs[m] + off, v);
     }
   }
 }
 
 hipError_t launch_gather_t(const uint16_t* src, int H, bool scaled, const int32_t* stok,
                            const float* sw, const int32_t* offsets, const int32_t* pcol,
-                           uint16_t* out, size_t pstride, int max_blocks, hipStream_t st) {
+                           uint16_t* out, int max_blocks, hipStream_t st) {
   dim3 grid(max_blocks, H / 64);
   if (scaled)
-    gather_t_kernel<true><<<grid, 256, 0, st>>>(src, H, stok, sw, offsets, pcol, out, pstride);
+    gather_t_kernel<true><<<grid, 256, 0, st>>>(src, H, stok, sw, offsets, pcol, out);
   else
-    gather_t_kernel<false><<<grid, 256, 0, st>>>(src, H, stok, sw, offsets, pcol, out, pstride);
+    gather_t_kernel<false><<<grid, 256, 0, st>>>(src, H, stok, sw, offsets, pcol, out);
   return hipGetLastError();
 }
 
-hipError_t launch_zero_pads(uint16_t* a, uint16_t* b, uint16_t* c, int N, size_t pstride,
-                            const int32_t* offsets, const int32_t* pcol, int max_blocks,
-                            hipStream_t st) {
-  zero_pads_kernel<<<max_blocks, 256, 0, st>>>(a, b, c, N, pstride, offsets, pcol);
+hipError_t launch_zero_pads(uint16_t* a, uint16_t* b, uint16_t* c, int N, const int32_t* offsets,
+                            const int32_t* pcol, hipStream_t st) {
+  zero_pads_kernel<<<kExperts, 256, 0, st>>>(a, b, c, N, offsets, pcol);
   return hipGetLastError();
 }
 
@@ -239,17 +251,18 @@ hipError_t launch_router_grad(const uint16_t* x, int H, const int32_t* stok,
 
 // ---------------------------------------------------------------- weight-gradient GEMM
 // C[e] (M x N, bf16, row-major) = A_e B_e^T, where A_e and B_e are expert e's
-// segments of the transposed copies A [M, pcols] and B [N, pcols] (the
-// reduction runs over the expert's sorted rows; pad columns are zero). An
+// segments of the transposed copies A [M, pcols] and B [N, pcols] in
+// 32-column blocks (the reduction runs over the expert's sorted rows; pad
+// columns are zero, and one step's operand rows are contiguous). An
 // expert with no rows gets a zero matrix. TM x TN tiles, WAVES waves as a
 // 2 x (WAVES / 2) grid, operands by DMA into an NS-stage LDS ring of
 // 32-column steps (both operands stored like the A tile of the DMA variant:
 // row r's 16-byte chunk g at position g ^ ((r >> 1) & 3)).
-template <int TM, int TN, int WAVES, int NS>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
+template <int TM, int TN, int WAVES, int NS, int OCC = 1>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(WAVES / 4 * OCC, WAVES / 4 * OCC)))
 void gemm_wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm, int M,
-                       int N, size_t pstride, const int32_t* __restrict__ pcol,
-                       uint16_t* __restrict__ C) {
+                       int N, const int32_t* __restrict__ pcol, uint16_t* __restrict__ C) {
   constexpr int WN = WAVES / 2;                    // waves along N
   constexpr int WTM = TM / 2, WTN = TN / WN;       // wave tile
   constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -257,7 +270,9 @@ void gemm_wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
   constexpr int AI = TM / 16 / WAVES, BI = TN / 16 / WAVES;  // DMA instructions per wave
   constexpr int PER = AI + BI;
   static_assert(AI >= 1 && BI >= 1 && FM >= 1 && FN >= 1, "tile shape");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  constexpr int CS = TN * 2 + 16;  // staged output row stride in bytes (padded against bank conflicts)
+  constexpr int SMEM = NS * STAGE > TM * CS ? NS * STAGE : TM * CS;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   const int mtn = M / TM, ntn = N / TN;
   // XCD-contiguous numbering: the blocks on one XCD (b % 8) take a contiguous
   // range of tiles, so an expert's tiles, which share operand rows, meet in
@@ -275,22 +290,25 @@ void gemm_wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
   // DMA sources: instruction i of this wave fills rows 16 (wave * AI + i) .. of the tile
   const uint16_t* asrc[AI];
   const uint16_t* bsrc[BI];
+  const size_t cb = (size_t)(c0 >> 5);  // first 32-column block of the segment
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
     const int row = (wave * AI + i) * 16 + (lane >> 2);
-    asrc[i] = A + (size_t)(m0 + row) * pstride + c0 + (((lane & 3) ^ ((row >> 1) & 3)) * 8);
+    asrc[i] = A + ((cb * M + m0 + row) << 5) + (((lane & 3) ^ ((row >> 1) & 3)) * 8);
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
     const int row = (wave * BI + i) * 16 + (lane >> 2);
-    bsrc[i] = Bm + (size_t)(n0 + row) * pstride + c0 + (((lane & 3) ^ ((row >> 1) & 3)) * 8);
+    bsrc[i] = Bm + ((cb * N + n0 + row) << 5) + (((lane & 3) ^ ((row >> 1) & 3)) * 8);
   }
   auto issue = [&](int kt) {
     uint8_t* st = smem + (kt % NS) * STAGE;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) dma16(asrc[i] + (size_t)kt * 32, st + (wave * AI + i) * 1024);
+    for (int i = 0; i < AI; ++i)
+      dma16(asrc[i] + ((size_t)kt * M << 5), st + (wave * AI + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < BI; ++i) dma16(bsrc[i] + (size_t)kt * 32, st + TA + (wave * BI + i) * 1024);
+    for (int i = 0; i < BI; ++i)
+      dma16(bsrc[i] + ((size_t)kt * N << 5), st + TA + (wave * BI + i) * 1024);
   };
   int aoff[FM], boff[FN];
 #pragma unroll
@@ -335,27 +353,37 @@ void gemm_wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restric
     wait_lgkmcnt0();
     asm volatile("" ::: "memory");
   }
-  // lane (r, g) of fragment (i, jn): row m0 + WTM wm + 16 i + r, columns
-  // n0 + WTN wn + 16 jn + 4 g .. + 3
-  uint16_t* Ce = C + (size_t)e * M * N;
+  // The output tile goes through LDS (over the drained ring) so that global stores
+  // are whole 16-byte chunks of contiguous rows. Lane (r, g) of fragment
+  // (i, jn) holds tile row WTM wm + 16 i + r, columns WTN wn + 16 jn + 4 g .. + 3.
+  __syncthreads();  // every wave is past its last read of the ring
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int row = m0 + wm * WTM + i * 16 + r;
+    const int row = wm * WTM + i * 16 + r;
 #pragma unroll
     for (int jn = 0; jn < FN; ++jn) {
-      const int n = n0 + wn * WTN + jn * 16 + 4 * g;
+      const int col = wn * WTN + jn * 16 + 4 * g;
       const f32x4 v = acc[i][jn];
-      *reinterpret_cast<u32x2*>(Ce + (size_t)row * N + n) =
+      *reinterpret_cast<u32x2*>(smem + row * CS + col * 2) =
           u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
   }
+  __syncthreads();
+  uint16_t* Ce = C + (size_t)e * M * N + (size_t)m0 * N + n0;
+  constexpr int CPR = TN / 8;  // 16-byte chunks per tile row
+  static_assert(TM * CPR % (WAVES * 64) == 0, "whole copy rounds");
+#pragma unroll
+  for (int it = 0; it < TM * CPR / (WAVES * 64); ++it) {
+    const int q = tid + it * WAVES * 64, row = q / CPR, c = q % CPR;
+    st16(Ce + (size_t)row * N + c * 8, ld16(smem + row * CS + c * 16));
+  }
 }
 
-hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, int M, int N, size_t pstride,
-                        const int32_t* pcol, uint16_t* C, hipStream_t st) {
+hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, int M, int N, const int32_t* pcol,
+                        uint16_t* C, hipStream_t st) {
   if (M % 256 || N % 256) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)kExperts * (M / 256) * (N / 256);
-  gemm_wgrad_kernel<256, 256, 8, 4><<<blocks, 512, 0, st>>>(A, B, M, N, pstride, pcol, C);
+  gemm_wgrad_kernel<256, 256, 8, 3><<<blocks, 512, 0, st>>>(A, B, M, N, pcol, C);
   return hipGetLastError();
 }
 

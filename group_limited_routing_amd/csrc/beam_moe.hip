@@ -71,7 +71,7 @@ Layout make_layout(const Shape& s) {
 struct BwdLayout {
   Layout f;
   size_t ssel, gu, d, part, dz, pcol, xt, gyt, ht, dgt, dut, total;
-  size_t pstride;  // row length of the transposed copies (columns)
+  size_t pstride;  // columns of the transposed copies (segments of 32-column blocks)
   int nparts;      // partial sums of h . q per sorted row
 };
 
@@ -525,7 +525,6 @@ beam_status backward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
   g.stok = B.stok;
   g.max_mtiles = L.max_mtiles;
   g.pcol = pcol;
-  g.pstride = BL.pstride;
   // g | u of every sorted row (and h transposed)
   g.a = x;
   g.w0 = w_gate;
@@ -569,17 +568,13 @@ beam_status backward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
     uint16_t* xt = (uint16_t*)(ws + BL.xt);
     uint16_t* gyt = (uint16_t*)(ws + BL.gyt);
     STAGE(BEAM_STAGE_BWD_TRANSPOSE, launch_gather_t((const uint16_t*)x, H, false, B.stok, B.sw,
-                                                    B.offsets, pcol, xt, BL.pstride, cblocks, st));
+                                                    B.offsets, pcol, xt, cblocks, st));
     STAGE(BEAM_STAGE_BWD_TRANSPOSE, launch_gather_t((const uint16_t*)dout, H, true, B.stok, B.sw,
-                                                    B.offsets, pcol, gyt, BL.pstride, cblocks, st));
-    STAGE(BEAM_STAGE_BWD_TRANSPOSE, launch_zero_pads(ht, dgt, dut, I, BL.pstride, B.offsets, pcol,
-                                                     cblocks, st));
-    STAGE(BEAM_STAGE_BWD_WGRAD, launch_wgrad(gyt, ht, H, I, BL.pstride, pcol,
-                                             (uint16_t*)grads->d_w_down, st));
-    STAGE(BEAM_STAGE_BWD_WGRAD, launch_wgrad(dgt, xt, I, H, BL.pstride, pcol,
-                                             (uint16_t*)grads->d_w_gate, st));
-    STAGE(BEAM_STAGE_BWD_WGRAD, launch_wgrad(dut, xt, I, H, BL.pstride, pcol,
-                                             (uint16_t*)grads->d_w_up, st));
+                                                    B.offsets, pcol, gyt, cblocks, st));
+    STAGE(BEAM_STAGE_BWD_TRANSPOSE, launch_zero_pads(ht, dgt, dut, I, B.offsets, pcol, st));
+    STAGE(BEAM_STAGE_BWD_WGRAD, launch_wgrad(gyt, ht, H, I, pcol, (uint16_t*)grads->d_w_down, st));
+    STAGE(BEAM_STAGE_BWD_WGRAD, launch_wgrad(dgt, xt, I, H, pcol, (uint16_t*)grads->d_w_gate, st));
+    STAGE(BEAM_STAGE_BWD_WGRAD, launch_wgrad(dut, xt, I, H, pcol, (uint16_t*)grads->d_w_up, st));
   }
   return BEAM_OK;
 }

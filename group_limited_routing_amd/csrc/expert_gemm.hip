@@ -1086,12 +1086,14 @@ void gemm_dma_kernel(GemmArgs p) {
 
 // Epilogues of modes 2 and 3 (lane (r, g) of fragment (fm, fn) holds row
 // row_base + 16 fm + r, columns 16 c + 4 g .. + 3 as in transposed_epilogue).
-// Transposed copies (h, dg, du) go to [I, pcols] matrices whose column of
-// sorted row q is p.pcol[e] + q - offsets[e] (each expert's rows a segment).
-__device__ __forceinline__ void store_col4(uint16_t* base, size_t pstride, int n, size_t col,
+// Transposed copies (h, dg, du) are [N, pcols] matrices whose column of
+// sorted row q is p.pcol[e] + q - offsets[e] (each expert's rows a segment),
+// stored in 32-column blocks: element (n, c) at ((c / 32) N + n) 32 + c % 32.
+__device__ __forceinline__ void store_col4(uint16_t* base, int N, int n, int col,
                                            const float (&v)[4]) {
+  uint16_t* p = base + ((((size_t)(col >> 5) * N) + n) << 5) + (col & 31);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) base[(size_t)(n + i) * pstride + col] = (uint16_t)f32_to_bf16_bits(v[i]);
+  for (int i = 0; i < 4; ++i) p[32 * i] = (uint16_t)f32_to_bf16_bits(v[i]);
 }
 
 template <int MODE, int FM, int FN>
@@ -1107,7 +1109,7 @@ __device__ __forceinline__ void backward_epilogue(const GemmArgs& p, const TileI
     const int row = row_base + fm * 16 + r;
     const bool valid = row < ti.rows;
     const size_t grow = (size_t)(ti.row0 + (valid ? row : 0));
-    const size_t col = tr ? (size_t)(p.pcol[ti.e] + (int)grow - p.offsets[ti.e]) : 0;
+    const int col = tr ? p.pcol[ti.e] + (int)grow - p.offsets[ti.e] : 0;
     if constexpr (MODE == 2) {
       constexpr int NF = FN / 2;
       if (valid) {
@@ -1122,7 +1124,7 @@ __device__ __forceinline__ void backward_epilogue(const GemmArgs& p, const TileI
             float h[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) h[i] = silu_f32(gv[i]) * uv[i];
-            store_col4((uint16_t*)p.tout0, p.pstride, n, col, h);
+            store_col4((uint16_t*)p.tout0, N, n, col, h);
           }
         }
       }
@@ -1154,8 +1156,8 @@ __device__ __forceinline__ void backward_epilogue(const GemmArgs& p, const TileI
           *reinterpret_cast<u32x2*>(out + grow * ld + N + n) =
               u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
           if (tr) {
-            store_col4((uint16_t*)p.tout0, p.pstride, n, col, dg);
-            store_col4((uint16_t*)p.tout1, p.pstride, n, col, du);
+            store_col4((uint16_t*)p.tout0, N, n, col, dg);
+            store_col4((uint16_t*)p.tout1, N, n, col, du);
           }
         }
       }

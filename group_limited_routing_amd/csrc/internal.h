@@ -76,10 +76,9 @@ struct GemmArgs {
   int max_mtiles;
   // backward pass only
   const void* a2;           // g | u rows of the recomputed gate/up pass
-  void* tout0;              // transposed outputs [N, pcols] (null: none)
+  void* tout0;              // transposed outputs [N, pcols] in 32-column blocks (null: none)
   void* tout1;
   const int32_t* pcol;      // first column of each expert's segment in them
-  size_t pstride;           // their row length (pcols)
   float* part;              // per-row partial sums of h . q, nparts per row
   int nparts;
 };
@@ -107,20 +106,21 @@ hipError_t launch_combine_residual(const void* y, const int32_t* inv, int T, int
                                    float keep, float add, void* stream_out, hipStream_t st);
 // backward pass (backward.hip)
 hipError_t launch_segment_cols(const int32_t* counts, int32_t* pcol, hipStream_t st);
+// Transposed copies [R, pcols] are stored in 32-column blocks: element (n, c)
+// at ((c / 32) R + n) 32 + c % 32.
 hipError_t launch_gather_t(const uint16_t* src, int H, bool scaled, const int32_t* stok,
                            const float* sw, const int32_t* offsets, const int32_t* pcol,
-                           uint16_t* out, size_t pstride, int max_blocks, hipStream_t st);
-hipError_t launch_zero_pads(uint16_t* a, uint16_t* b, uint16_t* c, int N, size_t pstride,
-                            const int32_t* offsets, const int32_t* pcol, int max_blocks,
-                            hipStream_t st);
+                           uint16_t* out, int max_blocks, hipStream_t st);
+hipError_t launch_zero_pads(uint16_t* a, uint16_t* b, uint16_t* c, int N, const int32_t* offsets,
+                            const int32_t* pcol, hipStream_t st);
 hipError_t launch_token_grad(const uint16_t* dxr, const int32_t* inv, const int32_t* idx,
                              const float* w, const float* s_sel, const float* part, int nparts,
                              float rsf, const float* router_w, int T, int k, int H,
                              float* dz_sorted, uint16_t* dx, hipStream_t st);
 hipError_t launch_router_grad(const uint16_t* x, int H, const int32_t* stok,
                               const int32_t* offsets, const float* dz, float* drw, hipStream_t st);
-hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, int M, int N, size_t pstride,
-                        const int32_t* pcol, uint16_t* C, hipStream_t st);
+hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, int M, int N, const int32_t* pcol,
+                        uint16_t* C, hipStream_t st);
 hipError_t launch_pack_t(const void* src, void* dst, int E, int rows, int cols, hipStream_t st);
 hipError_t launch_bias_step(float* bias, const int32_t* counts, float gamma, hipStream_t st);
 hipError_t launch_quant_x(const void* x, int x_f32, int T, int H, int k, uint8_t* xq, float* xs,

@@ -1046,6 +1046,12 @@ void gemm_dma_kernel(GemmArgs p) {
         for (int f = 0; f < FN; ++f) bfr[f] = ld16(st + boff[f]);
 #pragma unroll
         for (int i = 0; i < NF; ++i) af[i] = ld16(st + aoff[i]);
+        // Every fragment read is issued ahead of the multiplies: left to
+        // itself the scheduler reloads two A fragments at a time into the
+        // same registers and waits for each pair with the matrix core idle
+        // (3-5% of the 256-row tiles' time; the fp8 variants, HBM-bound and
+        // near the register limit, lose about 1% with it and keep the default).
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NF; ++i)
 #pragma unroll

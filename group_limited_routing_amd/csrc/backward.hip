@@ -34,7 +34,8 @@ hipError_t launch_segment_cols(const int32_t* counts, int32_t* pcol, hipStream_t
   return hipGetLastError();
 }
 
-// Expert owning column block cb (32 columns) of the segments, or -1 past the end.
+// Expert whose segment holds column col, or -1 past the last segment (an
+// empty expert's segment holds no column).
 __device__ __forceinline__ int segment_of(const int32_t* pcol, int col) {
   if (col >= pcol[kExperts]) return -1;
   int lo = 0, hi = kExperts - 1;  // largest e with pcol[e] <= col

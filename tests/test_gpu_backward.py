@@ -123,6 +123,17 @@ def test_backward_256_row_tiles():
     _full_compare("256 rows", _case(3200, 256, 256), 32)
 
 
+def test_backward_single_token_and_empty():
+    """T=1 (eight experts with one row each, the rest zero) and T=0."""
+    _full_compare("T=1", _case(1, 256, 256), 34)
+    dev = _dev()
+    cfg = _case(1, 256, 256)
+    x, rw, b = (t.to(dev) for t in workloads.make_small_inputs(cfg, 34))
+    pw = _packed(workloads.make_expert_weights(cfg, 34, dev))
+    g = _run(cfg, x[:0], rw, b, pw, torch.empty((0, 256), dtype=torch.bfloat16, device=dev))
+    assert g["dx"].shape == (0, 256)
+
+
 def test_backward_without_weight_grads_matches():
     dev = _dev()
     cfg = _case(200, 512, 512)

@@ -26,7 +26,8 @@ BEAM_LAYOUT_ROW_MAJOR, BEAM_LAYOUT_PACKED = 0, 1
 EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_forward",
             "beam_moe_forward_residual", "beam_moe_status_string", "beam_moe_profile_begin",
             "beam_moe_profile_end", "beam_moe_pack_weights", "beam_moe_backward_workspace_bytes",
-            "beam_moe_backward", "beam_moe_pack_weights_transposed", "beam_moe_update_bias")
+            "beam_moe_backward", "beam_moe_pack_weights_transposed", "beam_moe_update_bias",
+            "beam_moe_forward_shard")
 
 STAGES = ("router_logits", "select", "perm_hist", "perm_scan", "perm_scatter", "quant_x",
           "gateup", "quant_h", "down", "combine", "bwd_gateup", "bwd_down", "bwd_dx",
@@ -105,6 +106,9 @@ def lib():
         L.beam_moe_profile_end.restype = ctypes.c_int
         L.beam_moe_pack_weights.argtypes = [vp, vp, i32, i32, i32, i32, vp]
         L.beam_moe_pack_weights.restype = ctypes.c_int
+        L.beam_moe_forward_shard.argtypes = [cfgp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, vp, sz, vp]
+        L.beam_moe_forward_shard.restype = ctypes.c_int
         L.beam_moe_backward_workspace_bytes.argtypes = [cfgp, i32, i32]
         L.beam_moe_backward_workspace_bytes.restype = sz
         L.beam_moe_backward.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -257,11 +261,24 @@ def forward_residual(x, router_w, expert_bias, w_gate, w_up, w_down, stream_in, 
                     return_logits, workspace, stream, packed)
 
 
+def forward_shard(x, router_w, expert_bias, expert_begin, expert_end, w_gate, w_up, w_down, *,
+                  scales=None, n_group=8, topk_group=4, top_k=8, routed_scaling_factor=2.5,
+                  out=None, return_routing=False, workspace=None, stream=None, packed=False):
+    """One expert shard's share of the block: the weights (and scales) hold
+    experts [expert_begin, expert_end) only; returns the partial output
+    [T, H] (x's dtype) whose sum over a partition of the experts is the block
+    output. Other arguments as for forward()."""
+    return _forward(x, router_w, expert_bias, w_gate, w_up, w_down, None, scales, n_group,
+                    topk_group, top_k, routed_scaling_factor, out, return_routing, False,
+                    workspace, stream, packed, shard=(int(expert_begin), int(expert_end)))
+
+
 def _forward(x, router_w, expert_bias, w_gate, w_up, w_down, res, scales, n_group, topk_group,
              top_k, routed_scaling_factor, out, return_routing, return_logits, workspace,
-             stream, packed):
+             stream, packed, shard=None):
     T, H = x.shape
     E = router_w.shape[0]
+    n_w = E if shard is None else shard[1] - shard[0]  # experts held by the weight arrays
     I = w_gate.shape[1]
     dev = x.device
     wdt = (torch.bfloat16, torch.float8_e4m3fn, torch.uint8)
@@ -270,22 +287,22 @@ def _forward(x, router_w, expert_bias, w_gate, w_up, w_down, res, scales, n_grou
     _check(x, "x", (T, H), (torch.float32, torch.bfloat16), dev)
     _check(router_w, "router_w", (E, H), (torch.float32,), dev)
     _check(expert_bias, "expert_bias", (E,), (torch.float32,), dev)
-    _check(w_gate, "w_gate", (E, I, H // d), wdt, dev)
-    _check(w_up, "w_up", (E, I, H // d), (w_gate.dtype,), dev)
-    _check(w_down, "w_down", (E, H, I // d), (w_gate.dtype,), dev)
+    _check(w_gate, "w_gate", (n_w, I, H // d), wdt, dev)
+    _check(w_up, "w_up", (n_w, I, H // d), (w_gate.dtype,), dev)
+    _check(w_down, "w_down", (n_w, H, I // d), (w_gate.dtype,), dev)
     sg = su = sd = None
     if w_gate.dtype in (torch.float8_e4m3fn, torch.uint8):
         if scales is None:
             raise ValueError("quantised weights need (w_gate_scale, w_up_scale, w_down_scale)")
         sg, su, sd = scales
         if mx:
-            _check(sg, "w_gate_scale", (E, I, H // 32), (torch.uint8,), dev)
-            _check(su, "w_up_scale", (E, I, H // 32), (torch.uint8,), dev)
-            _check(sd, "w_down_scale", (E, H, I // 32), (torch.uint8,), dev)
+            _check(sg, "w_gate_scale", (n_w, I, H // 32), (torch.uint8,), dev)
+            _check(su, "w_up_scale", (n_w, I, H // 32), (torch.uint8,), dev)
+            _check(sd, "w_down_scale", (n_w, H, I // 32), (torch.uint8,), dev)
         else:
-            _check(sg, "w_gate_scale", (E, I), (torch.float32,), dev)
-            _check(su, "w_up_scale", (E, I), (torch.float32,), dev)
-            _check(sd, "w_down_scale", (E, H), (torch.float32,), dev)
+            _check(sg, "w_gate_scale", (n_w, I), (torch.float32,), dev)
+            _check(su, "w_up_scale", (n_w, I), (torch.float32,), dev)
+            _check(sd, "w_down_scale", (n_w, H), (torch.float32,), dev)
     cfg = make_config(H, I, E, n_group, topk_group, top_k, routed_scaling_factor, x.dtype,
                       w_gate.dtype, packed)
     if out is None:
@@ -300,7 +317,14 @@ def _forward(x, router_w, expert_bias, w_gate, w_up, w_down, res, scales, n_grou
     if return_logits:
         logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     ws = _workspace(cfg, T, dev, workspace)
-    if res is None:
+    if shard is not None:
+        st = lib().beam_moe_forward_shard(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w),
+                                          _ptr(expert_bias), shard[0], shard[1], _ptr(w_gate),
+                                          _ptr(w_up), _ptr(w_down), _ptr(sg), _ptr(su), _ptr(sd),
+                                          _ptr(out), _ptr(idx), _ptr(w), _ptr(counts), _ptr(ws),
+                                          ws.numel(), _stream(dev, stream))
+        where = "beam_moe_forward_shard"
+    elif res is None:
         st = lib().beam_moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w),
                                     _ptr(expert_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                     _ptr(sg), _ptr(su), _ptr(sd), _ptr(out), _ptr(idx), _ptr(w),

@@ -329,16 +329,29 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
 
 namespace {
 
-// The forward pass; with `res` set the final combine is the fused residual step.
+// Shift a per-expert array's base so that expert e (>= e0) is found at
+// e * stride from it: the arrays of an expert shard hold experts e0.. only.
+// Integer arithmetic: the shifted base itself is never dereferenced.
+const void* shard_base(const void* p, int e0, size_t stride_bytes) {
+  return p ? (const void*)((uintptr_t)p - (uintptr_t)e0 * stride_bytes) : nullptr;
+}
+
+// The forward pass; with `res` set the final combine is the fused residual
+// step; with an expert range [e0, e1) other than all experts it is one
+// expert shard's share (its weights hold experts e0 .. e1 - 1 only).
 beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
                          const float* router_w, const float* expert_bias, const void* w_gate,
                          const void* w_up, const void* w_down, const void* w_gate_scale,
                          const void* w_up_scale, const void* w_down_scale,
                          const beam_moe_residual* res, void* out, int32_t* topk_idx_out,
                          float* topk_w_out, int32_t* expert_counts_out, float* router_logits_out,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream, int e0 = 0,
+                         int e1 = kExperts) {
   const beam_status cs = check_config(cfg);
   if (cs != BEAM_OK) return cs;
+  if (e0 < 0 || e1 > kExperts || e0 >= e1) return BEAM_ERR_CONFIG;
+  const bool shard = e0 > 0 || e1 < kExperts;
+  if (shard && res) return BEAM_ERR_CONFIG;
   if (T < 0 || T > kMaxT) return BEAM_ERR_SHAPE;
   if (res) {
     if (!isfinite(res->norm_eps) || res->norm_eps < 0.f || res->step < 2) return BEAM_ERR_CONFIG;
@@ -368,13 +381,28 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
   float* w = topk_w_out ? topk_w_out : B.w;
   const int k = s.top_k;
   const int BM = use_stream_gemm(s) ? kStreamBM : (s.w_packed ? wide_bm(s) : kTiledBM);
+  if (shard) {
+    // weights, and fp8 / MXFP4 scales, of experts e0 .. e1 - 1 only
+    const size_t ih = (size_t)s.I * s.H;
+    const size_t wb = s.w_mx4 ? ih / 2 : (s.w_fp8 ? ih : ih * 2);
+    w_gate = shard_base(w_gate, e0, wb);
+    w_up = shard_base(w_up, e0, wb);
+    w_down = shard_base(w_down, e0, wb);
+    if (fp8) {
+      const size_t sg = s.w_mx4 ? ih / 32 : (size_t)s.I * 4, sd = s.w_mx4 ? ih / 32 : (size_t)s.H * 4;
+      w_gate_scale = shard_base(w_gate_scale, e0, sg);
+      w_up_scale = shard_base(w_up_scale, e0, sg);
+      w_down_scale = shard_base(w_down_scale, e0, sd);
+    }
+  }
 
   const beam_status rs = route_tokens(s, L, B, x, router_w, expert_bias, router_logits_out, idx, w,
                                       st);
   if (rs != BEAM_OK) return rs;
   STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(idx, T, k, B.chist, st));
   STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts, B.offsets, B.meta,
-                               B.tile_e, B.tile_r, B.e_tstart, B.e_ntiles, expert_counts_out, st));
+                               B.tile_e, B.tile_r, B.e_tstart, B.e_ntiles, expert_counts_out, st,
+                               e0, e1));
   STAGE(BEAM_STAGE_PERM_SCATTER, launch_perm_scatter(idx, w, T, k, s.rsf, B.cbase, B.offsets, B.stok, B.sw, B.inv, st));
 
   GemmArgs g{};
@@ -437,7 +465,10 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
     g.N = s.H;
     STAGE(BEAM_STAGE_DOWN, launch_down(s, g, st));
   }
-  if (res) {
+  if (shard) {
+    STAGE(BEAM_STAGE_COMBINE, launch_combine_shard(y, B.inv, idx, T, k, s.H, e0, e1, s.x_f32, out,
+                                                   st));
+  } else if (res) {
     const double kk = res->step;
     const float keep = (float)sqrt((kk - 1.0) / kk), add = (float)(1.0 / sqrt(kk));
     STAGE(BEAM_STAGE_COMBINE, launch_combine_residual(y, B.inv, T, k, s.H, s.x_f32, res->stream_in,
@@ -633,6 +664,20 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
   return forward_impl(cfg, T, x, router_w, expert_bias, w_gate, w_up, w_down, w_gate_scale,
                       w_up_scale, w_down_scale, nullptr, out, topk_idx_out, topk_w_out,
                       expert_counts_out, router_logits_out, workspace, workspace_bytes, stream);
+}
+
+beam_status beam_moe_forward_shard(const beam_moe_config* cfg, int32_t T, const void* x,
+                                  const float* router_w, const float* expert_bias,
+                                  int32_t expert_begin, int32_t expert_end, const void* w_gate,
+                                  const void* w_up, const void* w_down, const void* w_gate_scale,
+                                  const void* w_up_scale, const void* w_down_scale,
+                                  void* out_partial, int32_t* topk_idx_out, float* topk_w_out,
+                                  int32_t* expert_counts_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return forward_impl(cfg, T, x, router_w, expert_bias, w_gate, w_up, w_down, w_gate_scale,
+                      w_up_scale, w_down_scale, nullptr, out_partial, topk_idx_out, topk_w_out,
+                      expert_counts_out, nullptr, workspace, workspace_bytes, stream, expert_begin,
+                      expert_end);
 }
 
 beam_status beam_moe_forward_residual(const beam_moe_config* cfg, int32_t T, const void* x,

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace beam {
 
 // Row tile (tokens per M-tile) of the two expert-GEMM variants.
@@ -47,10 +49,11 @@ hipError_t launch_select(const float* z, int nparts, size_t pstride, float* zout
                          int T, int n_group, int topk_group, int top_k, int32_t* idx, float* w,
                          float* s_sel, hipStream_t st);
 hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int32_t* chist, hipStream_t st);
+// Tiles only for experts in [e0, e1) (all experts by default).
 hipError_t launch_perm_scan(const int32_t* chist, int nchunks, int BM, int32_t* cbase,
                             int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,
                             int32_t* tile_r, int32_t* e_tstart, int32_t* e_ntiles,
-                            int32_t* counts_out, hipStream_t st);
+                            int32_t* counts_out, hipStream_t st, int e0 = 0, int e1 = kExperts);
 hipError_t launch_perm_scatter(const int32_t* idx, const float* w, int T, int k, float rsf,
                                const int32_t* cbase, const int32_t* offsets, int32_t* stok,
                                float* sw, int32_t* inv, hipStream_t st);
@@ -98,6 +101,10 @@ hipError_t launch_pack_mx_scales(const uint8_t* src, uint8_t* dst, int E, int ro
                                  hipStream_t st);
 hipError_t launch_combine(const void* y, const int32_t* inv, int T, int k, int H, int out_f32,
                           void* out, hipStream_t st);
+// an expert shard's share of the output (slots with experts in [e0, e1))
+hipError_t launch_combine_shard(const void* y, const int32_t* inv, const int32_t* idx, int T,
+                                int k, int H, int e0, int e1, int out_f32, void* out,
+                                hipStream_t st);
 // Largest hidden size of the fused combine + residual step (a token's row is
 // held in the registers of one workgroup).
 constexpr int kResidualMaxH = 16384;

@@ -68,7 +68,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
 //   tile_e[m] = expert, tile_r[m] = first sorted row; meta[0] = tile count;
 //   e_tstart[e], e_ntiles[e] = first M-tile of expert e and its tile count.
 __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restrict__ chist,
-                                                        int nchunks, int BM,
+                                                        int nchunks, int BM, int e0, int e1,
                                                         int32_t* __restrict__ cbase,
                                                         int32_t* __restrict__ counts,
                                                         int32_t* __restrict__ offsets,
@@ -91,7 +91,8 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restric
   const int off = block_exclusive_scan(run, wsum);
   offsets[e] = off;
   if (e == kExperts - 1) offsets[kExperts] = off + run;
-  const int mt = (run + BM - 1) / BM;
+  // experts outside [e0, e1) keep their place in the sorted order but get no tiles
+  const int mt = (e >= e0 && e < e1) ? (run + BM - 1) / BM : 0;
   const int ts = block_exclusive_scan(mt, wsum);
   e_tstart[e] = ts;
   e_ntiles[e] = mt;
@@ -137,9 +138,62 @@ hipError_t launch_perm_hist(const int32_t* idx, int T, int k, int32_t* chist, hi
 hipError_t launch_perm_scan(const int32_t* chist, int nchunks, int BM, int32_t* cbase,
                             int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,
                             int32_t* tile_r, int32_t* e_tstart, int32_t* e_ntiles,
-                            int32_t* counts_out, hipStream_t st) {
-  perm_scan_kernel<<<1, 256, 0, st>>>(chist, nchunks, BM, cbase, counts, offsets, meta, tile_e,
-                                      tile_r, e_tstart, e_ntiles, counts_out);
+                            int32_t* counts_out, hipStream_t st, int e0, int e1) {
+  perm_scan_kernel<<<1, 256, 0, st>>>(chist, nchunks, BM, e0, e1, cbase, counts, offsets, meta,
+                                      tile_e, tile_r, e_tstart, e_ntiles, counts_out);
+  return hipGetLastError();
+}
+
+// One expert shard's share of the output: out[t] = sum over the slots j
+// whose expert lies in [e0, e1) of y_perm[inv[t, j]] (fp32, ascending j; a
+// token with no expert in the shard gets zeros). One thread per 8 values.
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_shard_kernel(const uint16_t* __restrict__ y,
+                                                            const int32_t* __restrict__ inv,
+                                                            const int32_t* __restrict__ idx,
+                                                            int T, int k, int H, int e0, int e1,
+                                                            OT* __restrict__ out) {
+  const int vpr = H / 8;
+  const long long v = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (v >= (long long)T * vpr) return;
+  const int t = (int)(v / vpr), c = (int)(v % vpr);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[(size_t)t * k + j];
+    if (e < e0 || e >= e1) continue;
+    const u32x4 q = *reinterpret_cast<const u32x4*>(y + (size_t)inv[(size_t)t * k + j] * H + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_bits_to_f32(q[i] & 0xffffu);
+      acc[2 * i + 1] += bf16_bits_to_f32(q[i] >> 16);
+    }
+  }
+  OT* o = out + (size_t)t * H + c * 8;
+  if constexpr (sizeof(OT) == 4) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<u32x4*>(o + 4 * h) =
+          u32x4{__float_as_uint(acc[4 * h]), __float_as_uint(acc[4 * h + 1]),
+                __float_as_uint(acc[4 * h + 2]), __float_as_uint(acc[4 * h + 3])};
+  } else {
+    *reinterpret_cast<u32x4*>(o) = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  }
+}
+
+hipError_t launch_combine_shard(const void* y, const int32_t* inv, const int32_t* idx, int T,
+                                int k, int H, int e0, int e1, int out_f32, void* out,
+                                hipStream_t st) {
+  const long long n = (long long)T * (H / 8);
+  const int blocks = (int)((n + 255) / 256);
+  if (out_f32)
+    combine_shard_kernel<float><<<blocks, 256, 0, st>>>((const uint16_t*)y, inv, idx, T, k, H, e0,
+                                                        e1, (float*)out);
+  else
+    combine_shard_kernel<uint16_t><<<blocks, 256, 0, st>>>((const uint16_t*)y, inv, idx, T, k, H,
+                                                           e0, e1, (uint16_t*)out);
   return hipGetLastError();
 }
 

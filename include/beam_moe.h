@@ -192,6 +192,33 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
                              void* stream);
 
 /*
+ * One expert shard's share of the block, for expert parallelism (launch post
+ * "Introducing Beam", section "Multi-GPU and multi-node": each expert lives
+ * on one device; transformers model doc "Beam": ep_size). The routing is
+ * computed over all experts exactly as in beam_moe_forward; the expert GEMMs
+ * run only for experts [expert_begin, expert_end), whose weights are the only
+ * ones given: w_gate, w_up [n, I, H], w_down [n, H, I] and their scales (same
+ * dtypes and layouts as beam_moe_forward) for n = expert_end - expert_begin,
+ * expert expert_begin first.
+ *   out_partial[t] = rsf * sum over the slots j of token t whose expert lies
+ *                    in the range of w[t, j] * FFN_e(x[t])   ([T, H], x dtype;
+ *                    zeros for a token with no expert in the range).
+ * The shards' partial outputs of a partition of the 256 experts sum to the
+ * block output (up to the rounding of each partial sum to the output dtype).
+ * Routing outputs (nullable) are those of all experts. Workspace as for
+ * beam_moe_forward. Errors as for beam_moe_forward; BEAM_ERR_CONFIG unless
+ * 0 <= expert_begin < expert_end <= 256.
+ */
+beam_status beam_moe_forward_shard(const beam_moe_config* cfg, int32_t T, const void* x,
+                                  const float* router_w, const float* expert_bias,
+                                  int32_t expert_begin, int32_t expert_end, const void* w_gate,
+                                  const void* w_up, const void* w_down, const void* w_gate_scale,
+                                  const void* w_up_scale, const void* w_down_scale,
+                                  void* out_partial, int32_t* topk_idx_out, float* topk_w_out,
+                                  int32_t* expert_counts_out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * The block followed by its place in Beam's residual stream, fused into the
  * final combine (launch post "Introducing Beam", section "Residual Stream";
  * model doc "Beam", "Overview": depth-scaled residual and sandwich norm):

@@ -215,6 +215,24 @@ def test_backward_checks(L):
     assert ub(v(FAKE + 4), v(FAKE), 256, 1e-3, None) == gl.BEAM_ERR_ALIGN
 
 
+def test_shard_checks(L):
+    """Expert shard: 0 <= begin < end <= 256; otherwise the forward's checks."""
+    c = beam_cfg()
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+
+    def shard(b, e, T=8, **over):
+        p = dict(x=FAKE, rw=FAKE, b=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, out=FAKE, ws=FAKE)
+        p.update(over)
+        return L.beam_moe_forward_shard(ctypes.byref(c), T, v(p["x"]), v(p["rw"]), v(p["b"]), b, e,
+                                        v(p["wg"]), v(p["wu"]), v(p["wd"]), None, None, None,
+                                        v(p["out"]), None, None, None, v(p["ws"]), 1 << 40, None)
+    for b, e in [(-1, 32), (0, 0), (32, 32), (64, 32), (0, 257), (255, 300)]:
+        assert shard(b, e) == gl.BEAM_ERR_CONFIG, (b, e)
+    assert shard(0, 32, out=None) == gl.BEAM_ERR_NULL
+    assert shard(0, 32, wg=FAKE + 4) == gl.BEAM_ERR_ALIGN
+    assert shard(224, 256, T=0, x=None, out=None, ws=None) == gl.BEAM_OK
+
+
 def test_workspace_size(L):
     c = beam_cfg()
     need = gl.workspace_bytes(c, 64)
@@ -261,7 +279,7 @@ def test_library_links_every_kernel(L):
     for kernel in ["gemm_dma4_kernel", "router_logits_kernel", "router_split_kernel", "router_x3_kernel", "select_kernel", "perm_hist_kernel", "perm_scan_kernel",
                    "perm_scatter_kernel", "gemm_stream_kernel", "gemm_tiled_kernel",
                    "gemm_wide_kernel", "gemm_dma_kernel", "gemm_dma8_kernel", "gemm_stream4_kernel",
-                   "combine_kernel", "combine_residual_kernel", "pack_mx_scales_kernel",
+                   "combine_kernel", "combine_residual_kernel", "combine_shard_kernel", "pack_mx_scales_kernel",
                    "segment_cols_kernel", "gather_t_kernel", "zero_pads_kernel",
                    "token_grad_kernel", "router_grad_kernel", "gemm_wgrad_kernel",
                    "pack_t_kernel", "bias_step_kernel", "quant_x_kernel",

@@ -326,6 +326,51 @@ def backward_line(cfg, dev, weights, steps, packed=None):
     return out
 
 
+def ep_shard_line(dev, bench, gpus=8, steps=50):
+    """One of `gpus` expert shards at Beam's decode shape: the tokens of
+    `gpus` x 64-token decode batches are routed over all experts and this
+    shard (experts 0 .. 256 / gpus - 1, its weights only) runs its share."""
+    import torch
+    import group_limited_routing_amd as gl
+    import workloads
+    cfg = dict(workloads.workload("decode"), T=64 * gpus)
+    e1 = cfg["n_experts"] // gpus
+    x, rw, b = (t.to(dev) for t in workloads.make_small_inputs(cfg, 0))
+    w = {k: bench.pw[k][:e1] for k in ("w_gate", "w_up", "w_down")}
+    r = gl.route(x, rw, b, return_counts=True)
+    cnt = r["expert_counts"].cpu()[:e1]
+    active, pairs = int((cnt > 0).sum()), int(cnt.sum())
+    c = gl.make_config(cfg["hidden"], cfg["intermediate"], x_dtype=x.dtype, w_dtype=w["w_gate"].dtype,
+                       packed=True)
+    ws = torch.empty(gl.workspace_bytes(c, cfg["T"]), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+
+    def step():
+        gl.forward_shard(x, rw, b, 0, e1, w["w_gate"], w["w_up"], w["w_down"], packed=True,
+                         out=out, workspace=ws)
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    gl.profile_begin(["gateup"])
+    e0_, e1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0_.record()
+    for _ in range(steps):
+        step()
+    e1_.record()
+    torch.cuda.synchronize()
+    prof = gl.profile_end()
+    ms = e0_.elapsed_time(e1_) / steps
+    gu_ms = prof["gateup"][0] / prof["gateup"][1]
+    H, I = cfg["hidden"], cfg["intermediate"]
+    gb = active * 2 * I * H * 2 + pairs * (H + I) * 2
+    return {"workload": f"expert shard 0-{e1 - 1} of {gpus} at decode: {cfg['T']} tokens "
+                        f"({gpus} x 64) routed over all experts, this shard's {pairs} pairs "
+                        f"on {active} active experts, bf16 weights (its {e1} experts only)",
+            "ms_per_step": round(ms, 4), "steps": steps,
+            "roofline": dict(roofline(gb, 4.0 * pairs * H * I, gu_ms / 1e3, "bf16"),
+                             kernel="gate/up", launch_ms=round(gu_ms, 4), algorithmic_bytes=gb)}
+
+
 def cpu_baseline(cfg, bench, n_tokens):
     """The oracle on the first n_tokens tokens of the same inputs (float64)."""
     import numpy as np
@@ -422,7 +467,7 @@ def write_traffic(fetch_dir, write_dir, workload):
     hbm = (f["kib"] * f["factor"] + w["kib"] * w["factor"]) * 1024
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <dir> -o run --output-format csv "
            f"-- python3 /root/repo/bench.py --workload {workload} --steps 3 --warmup 1 --no-prefill "
-           "--no-residual --no-backward --no-cpu-baseline --calibrate-copy")
+           "--no-residual --no-backward --no-shard --no-cpu-baseline --calibrate-copy")
     path = os.path.join(ROOT, "profiles", f"gateup_{workload}_counters.txt")
     with open(path, "w") as fh:
         fh.write(f"# HBM traffic of the gate/up grouped GEMM, workload {workload}, one MI355X\n")
@@ -459,6 +504,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward pass at the prefill shape")
     ap.add_argument("--backward-steps", type=int, default=10)
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip timing one expert shard of 8 at the decode shape")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens the oracle runs on (default: 64, MXFP4 weights 4; ~10-30 s)")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -550,6 +597,8 @@ def main():
                       "stages_ms": pres["stages_ms"]},
         }
         del pb
+    if args.workload == "decode" and not args.no_shard:
+        line["ep_shard"] = ep_shard_line(dev, bench)
     if args.workload == "decode" and not args.no_backward:
         line["backward"] = backward_line(workloads.workload("prefill"), dev, bench.w,
                                          args.backward_steps, bench.pw)

@@ -149,6 +149,7 @@ Shape shape_of(const beam_moe_config* c, int32_t T) {
   // fp8 and MXFP4 weights share the E4M3 activation path
   s.w_fp8 = c->w_dtype == BEAM_FP8_E4M3 || c->w_dtype == BEAM_MXFP4;
   s.w_mx4 = c->w_dtype == BEAM_MXFP4;
+  s.n_run = s.E;
   s.w_packed = c->w_layout == BEAM_LAYOUT_PACKED;
   return s;
 }
@@ -370,7 +371,8 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
       misaligned(workspace) ||
       (fp8 && (misaligned(w_gate_scale) || misaligned(w_up_scale) || misaligned(w_down_scale))))
     return BEAM_ERR_ALIGN;
-  const Shape s = shape_of(cfg, T);
+  Shape s = shape_of(cfg, T);
+  s.n_run = e1 - e0;
   const Layout L = make_layout(s);
   if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
 

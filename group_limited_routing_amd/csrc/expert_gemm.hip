@@ -1553,7 +1553,10 @@ template <int MODE, typename AT, bool FP8, bool PACKED>
 static void launch_stream(const Shape& s, const GemmArgs& g, hipStream_t st) {
   constexpr int D = 2;
   const int per = (MODE == 0) ? 32 : 64;  // columns per workgroup per unit of FN
-  const int fn = (g.N % (8 * per) == 0) ? 8 : (g.N % (4 * per) == 0) ? 4 : 2;
+  int fn = (g.N % (8 * per) == 0) ? 8 : (g.N % (4 * per) == 0) ? 4 : 2;
+  // Few experts running (an expert shard): narrower workgroups, so that
+  // about 1024 stream weights at once (one M-tile per expert at decode).
+  while (fn > 2 && (long long)s.n_run * (g.N / (fn * per)) < 1024) fn /= 2;
   dim3 grid(mtile_bound(s, kStreamBM) * (g.N / (fn * per)));
   if (fn == 8)
     gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, D><<<grid, 256, 0, st>>>(g);

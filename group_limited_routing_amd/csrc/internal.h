@@ -20,6 +20,7 @@ struct Shape {
   int w_fp8;   // 1: fp8 e4m3 weights with per-row scales
   int w_packed;  // 1: weights in the MFMA fragment layout
   int w_mx4;     // 1: MXFP4 weights (w_fp8 is set too: E4M3 activations)
+  int n_run;     // experts whose GEMMs run (E, or an expert shard's count)
 };
 
 // Byte offsets of each workspace region (all 256-byte aligned).

@@ -55,6 +55,8 @@ WEIGHT_BYTES = {"bf16": 2, "fp8": 1, "mxfp4": 0.5 + 1 / 32}
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 KERNEL_SOURCES = ["group_limited_routing_amd/csrc/expert_gemm.hip",
                   "group_limited_routing_amd/csrc/common.h"]
+WGRAD_SOURCES = ["group_limited_routing_amd/csrc/backward.hip",
+                 "group_limited_routing_amd/csrc/common.h"]
 COPY_CAL_KIB = 1 << 20          # the calibration copy moves 1 GiB each way
 
 
@@ -79,9 +81,9 @@ def gateup_kernel(cfg):
     return f"gemm_wide_kernel<0, {xt}, false, {bm}>"
 
 
-def kernel_source_sha():
+def kernel_source_sha(paths=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -133,10 +135,11 @@ def roofline(bytes_, flops, seconds, wdt, traffic=None):
             "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS[wdt], 4), "traffic": traffic}
 
 
-def stored_traffic(workload):
-    """HBM bytes per gate/up launch from the committed counter summary, or None
-    (missing, or counters taken on other kernel sources)."""
-    path = os.path.join(ROOT, "profiles", f"gateup_{workload}_counters.txt")
+def stored_traffic(workload, name="gateup", sources=KERNEL_SOURCES, key="hbm_bytes_per_launch"):
+    """HBM bytes per gate/up launch (or another stored figure) from the
+    committed counter summary, or None (missing, or counters taken on other
+    kernel sources)."""
+    path = os.path.join(ROOT, "profiles", f"{name}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -145,10 +148,10 @@ def stored_traffic(workload):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha") != kernel_source_sha():
+    if vals.get("kernel_source_sha") != kernel_source_sha(sources):
         return None
     try:
-        return int(float(vals["hbm_bytes_per_launch"]))
+        return int(float(vals[key]))
     except (KeyError, ValueError):
         return None
 
@@ -314,7 +317,10 @@ def backward_line(cfg, dev, weights, steps, packed=None):
     # roofline of the longest stage (its launches in one step)
     name = max(work, key=lambda k: per_step.get(k, 0.0))
     by, fl = work[name]
-    rl = roofline(by, fl, per_step[name] / 1e3, "bf16")
+    traffic = None
+    if name == "bwd_wgrad":
+        traffic = stored_traffic("backward", "wgrad", WGRAD_SOURCES, "hbm_bytes_per_step")
+    rl = roofline(by, fl, per_step[name] / 1e3, "bf16", traffic)
     out = {"workload": f"backward of {describe(cfg)}; gradients of x, the router and all "
                        "expert weights (bf16), output gradient N(0, 1)",
            "value": round(cfg["T"] / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
@@ -444,6 +450,44 @@ def _counter_rows(d):
     return rows
 
 
+def write_wgrad_traffic(fetch_dir, write_dir):
+    """HBM bytes of the backward's weight-gradient launches per step (three
+    launches, per-dispatch counters scaled as in write_traffic), from passes
+    over the default decode run with its backward line."""
+    out = {}
+    for name, d in (("fetch", fetch_dir), ("write", write_dir)):
+        rows = _counter_rows(d)
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        wg = [r for r in rows if "gemm_wgrad_kernel" in r["Kernel_Name"]]
+        if not wg:
+            raise SystemExit(f"no weight-gradient dispatches in {d}")
+        out[name] = {"copy_kib": copy, "factor": COPY_CAL_KIB / copy,
+                     "kib": sum(float(r["Counter_Value"]) for r in wg) / len(wg), "n": len(wg),
+                     "kernel": wg[0]["Kernel_Name"]}
+    f, w = out["fetch"], out["write"]
+    per_launch = (f["kib"] * f["factor"] + w["kib"] * w["factor"]) * 1024
+    cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <dir> -o run --output-format csv "
+           "-- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-prefill --no-residual "
+           "--no-shard --no-cpu-baseline --calibrate-copy --backward-steps 2")
+    path = os.path.join(ROOT, "profiles", "wgrad_backward_counters.txt")
+    with open(path, "w") as fh:
+        fh.write("# HBM traffic of the backward's weight-gradient GEMMs (prefill shape, all\n"
+                 "# expert weights), one MI355X\n# commands (one counter per pass):\n")
+        fh.write("#   " + cmd.format(c="FETCH_SIZE") + "\n")
+        fh.write("#   " + cmd.format(c="WRITE_SIZE") + "\n")
+        fh.write("#   python3 bench.py --wgrad-traffic <fetch dir> <write dir>\n")
+        fh.write(f"kernel = {f['kernel']}\n")
+        fh.write(f"dispatches = {f['n']}\n")
+        fh.write(f"fetch_kib_per_dispatch = {f['kib']:.1f}\n")
+        fh.write(f"write_kib_per_dispatch = {w['kib']:.1f}\n")
+        fh.write(f"fetch_factor = {f['factor']:.4f}\n")
+        fh.write(f"write_factor = {w['factor']:.4f}\n")
+        fh.write(f"hbm_bytes_per_launch = {per_launch:.0f}\n")
+        fh.write(f"hbm_bytes_per_step = {3 * per_launch:.0f}\n")
+        fh.write(f"kernel_source_sha = {kernel_source_sha(WGRAD_SOURCES)}\n")
+    print(open(path).read())
+
+
 def write_traffic(fetch_dir, write_dir, workload):
     """Turn one FETCH_SIZE pass and one WRITE_SIZE pass (rocprofv3 --pmc, KiB per
     dispatch) over `bench.py --workload W --no-prefill --calibrate-copy` into
@@ -511,6 +555,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--wgrad-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
 
     if args.summarize:
@@ -518,6 +563,9 @@ def main():
         return 0
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.workload)
+        return 0
+    if args.wgrad_traffic:
+        write_wgrad_traffic(args.wgrad_traffic[0], args.wgrad_traffic[1])
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:

@@ -569,9 +569,9 @@ def main():
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py measures one GPU: the MoE block here runs on a single MI355X "
-              "(expert-parallel sharding across GPUs is not part of this build); "
-              "run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no cross-GPU exchange (one expert "
+              "shard's compute is timed on one GPU in the ep_shard line); run with --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import torch

@@ -893,8 +893,10 @@ void gemm_wide_kernel(GemmArgs p) {
 // ahead, so roughly three stages of loads are in flight while one is
 // computed. Waits are explicit: before stage kt is read, vmcnt leaves only
 // the DMAs of the later stages outstanding, and a raw barrier publishes every
-// wave's stage-kt DMAs. Each wave consumes its LDS reads (its MFMAs need
-// them) before the barrier that lets a stage buffer be refilled. A wave
+// wave's stage-kt DMAs. Each wave has every LDS read of a stage completed
+// before the barrier that lets that stage buffer be refilled. Fragment reads
+// run a batch ahead of the MFMAs (see the k loop), so the matrix core keeps
+// working while the next fragments arrive. A wave
 // whose rows are partly past the expert's last row runs a copy of the loop
 // that reads and multiplies only its first FM/4 or FM/2 fragments (none if
 // no row is live), so an expert slightly over a tile boundary costs little
@@ -1030,35 +1032,98 @@ void gemm_dma_kernel(GemmArgs p) {
     constexpr int PER = decltype(al_c)::value + 2;  // this wave's DMAs per stage
 #pragma unroll
     for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0, al_c);
-    for (int kt = 0; kt < nk; ++kt) {
-      // stage kt done for this wave: at most the later issued stages outstanding
-      if (kt + NS - 2 < nk)
-        wait_vmcnt<(NS - 2) * PER>();
-      else
-        wait_vmcnt<0>();
-      barrier_only();  // ... and for every wave; all reads of kt - 1 retired
-      asm volatile("" ::: "memory");
-      if (kt + NS - 1 < nk) issue(kt + NS - 1, al_c);  // refills the slot read at kt - 1
-      if constexpr (NF > 0) {
+    if constexpr (NF > 0) {
+      // Fragment reads run one batch ahead of the multiplies: the A fragments
+      // of batch b + 1 are read while the MFMAs of batch b execute, and the B
+      // fragments and first A batch of step kt + 1 while the last batch of
+      // step kt executes (B double-buffered). Each wait for a batch's reads
+      // then comes after they have had a batch of MFMAs to land.
+      constexpr int AB = NF >= 2 ? 2 : 1;  // A fragments per batch
+      constexpr int NB = NF / AB;
+      u32x4 af[NF], bq0[FN], bq1[FN];
+      auto wait_stage = [&](int s) {  // stage s landed for this wave
+        if (s + NS - 2 < nk)
+          wait_vmcnt<(NS - 2) * PER>();
+        else
+          wait_vmcnt<0>();
+      };
+      auto batch = [&](int b0, const u32x4(&bq)[FN]) {
+#pragma unroll
+        for (int i = b0; i < b0 + AB; ++i)
+#pragma unroll
+          for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_op(bq[jn], af[i], acc[i][jn]);
+      };
+      auto step = [&](int kt, const u32x4(&bc)[FN], u32x4(&bn)[FN], auto more_c) {
+        constexpr bool MORE = decltype(more_c)::value;
         const uint8_t* st = smem + (kt % NS) * STAGE;
-        u32x4 af[NF], bfr[FN];
 #pragma unroll
-        for (int f = 0; f < FN; ++f) bfr[f] = ld16(st + boff[f]);
+        for (int b = 0; b < NB - 1; ++b) {
+          batch(b * AB, bc);
 #pragma unroll
-        for (int i = 0; i < NF; ++i) af[i] = ld16(st + aoff[i]);
-        // Every fragment read is issued ahead of the multiplies: left to
-        // itself the scheduler reloads two A fragments at a time into the
-        // same registers and waits for each pair with the matrix core idle
-        // (3-5% of the 256-row tiles' time; the fp8 variants, HBM-bound and
-        // near the register limit, lose about 1% with it and keep the default).
-        __builtin_amdgcn_sched_barrier(0);
+          for (int i = (b + 1) * AB; i < (b + 2) * AB; ++i) af[i] = ld16(st + aoff[i]);
+          // one read after each of the first AB MFMAs, the rest of the batch after
 #pragma unroll
-        for (int i = 0; i < NF; ++i)
+          for (int i = 0; i < AB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, AB * FN - AB, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (MORE) {
+          // every read of slot kt is done (its last batch is in registers), so
+          // after the barrier the slot can be refilled and step kt + 1 read
+          asm volatile("" ::: "memory");
+          wait_lgkmcnt0();
+          wait_stage(kt + 1);
+          barrier_only();
+          asm volatile("" ::: "memory");
+          if (kt + NS < nk) issue(kt + NS, al_c);
+          __builtin_amdgcn_sched_barrier(0);
+          const uint8_t* sn = smem + ((kt + 1) % NS) * STAGE;
+          batch((NB - 1) * AB, bc);
 #pragma unroll
-          for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_op(bfr[jn], af[i], acc[i][jn]);
-      }
-      wait_lgkmcnt0();
+          for (int f = 0; f < FN; ++f) bn[f] = ld16(sn + boff[f]);
+#pragma unroll
+          for (int i = 0; i < AB; ++i) af[i] = ld16(sn + aoff[i]);
+#pragma unroll
+          for (int i = 0; i < FN + AB; ++i) {
+            if (i < AB * FN) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if (FN + AB < AB * FN)
+            __builtin_amdgcn_sched_group_barrier(0x008, AB * FN - FN - AB, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          batch((NB - 1) * AB, bc);
+        }
+      };
+      wait_stage(0);
+      barrier_only();
       asm volatile("" ::: "memory");
+      if (NS - 1 < nk) issue(NS - 1, al_c);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) bq0[f] = ld16(smem + boff[f]);
+#pragma unroll
+      for (int i = 0; i < AB; ++i) af[i] = ld16(smem + aoff[i]);
+      // nk is a multiple of 4: steps in pairs, B buffers alternating
+      for (int kt = 0; kt < nk - 2; kt += 2) {
+        step(kt, bq0, bq1, std::true_type{});
+        step(kt + 1, bq1, bq0, std::true_type{});
+      }
+      step(nk - 2, bq0, bq1, std::true_type{});
+      step(nk - 1, bq1, bq0, std::false_type{});
+    } else {
+      // no live rows: the wave only loads and passes the same barriers
+      for (int kt = 0; kt < nk; ++kt) {
+        if (kt + NS - 2 < nk)
+          wait_vmcnt<(NS - 2) * PER>();
+        else
+          wait_vmcnt<0>();
+        barrier_only();
+        asm volatile("" ::: "memory");
+        if (kt + NS - 1 < nk) issue(kt + NS - 1, al_c);
+      }
     }
   };
   // fragments of this wave that hold live rows, and its A row groups with

@@ -60,6 +60,11 @@ WGRAD_SOURCES = ["group_limited_routing_amd/csrc/backward.hip",
 COPY_CAL_KIB = 1 << 20          # the calibration copy moves 1 GiB each way
 
 
+
+def progress(msg):
+    """One line on stderr per phase, so that long runs show where they are."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
 def gateup_kernel(cfg):
     """Name of the kernel the library launches for the gate/up pass of this
     workload with packed weights (same rules as its launcher)."""
@@ -509,7 +514,8 @@ def write_traffic(fetch_dir, write_dir, workload):
                      "n": len(gu), "kernel": kernels[0]}
     f, w = out["fetch"], out["write"]
     hbm = (f["kib"] * f["factor"] + w["kib"] * w["factor"]) * 1024
-    cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <dir> -o run --output-format csv "
+    cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --kernel-include-regex 'gemm|copyBuffer' "
+           "-d <dir> -o run --output-format csv "
            f"-- python3 /root/repo/bench.py --workload {workload} --steps 3 --warmup 1 --no-prefill "
            "--no-residual --no-backward --no-shard --no-cpu-baseline --calibrate-copy")
     path = os.path.join(ROOT, "profiles", f"gateup_{workload}_counters.txt")
@@ -584,7 +590,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     cfg = workloads.workload(args.workload)
+    progress(f"{args.workload}: inputs and weights")
     bench = Bench(cfg, dev)
+    progress(f"{args.workload}: {args.warmup} warmup + {args.steps} timed steps")
     res = bench.run(args.steps, args.warmup)
     wdt = "fp8" if cfg["w_dtype"] in ("fp8", "mxfp4") else "bf16"
     gb, gf = gateup_work(cfg, bench.active)
@@ -619,6 +627,7 @@ def main():
         # the same block with the fused post-norm + depth-scaled residual step
         # (the MoE of the last layer: step 105)
         bench.use_residual(105)
+        progress("fused residual step")
         rres = bench.run(min(args.steps, 50), 3)
         bench.residual = None
         line["fused_residual"] = {
@@ -628,6 +637,7 @@ def main():
             "plain_combine_ms": res["stages_ms"].get("combine")}
     if args.workload == "decode" and not args.no_prefill:
         pcfg = workloads.workload("prefill")
+        progress("prefill")
         pb = Bench(pcfg, dev, weights=bench.w, packed=bench.pw)
         pres = pb.run(args.prefill_steps, 3)
         pgb, pgf = gateup_work(pcfg, pb.active)
@@ -646,13 +656,16 @@ def main():
         }
         del pb
     if args.workload == "decode" and not args.no_shard:
+        progress("expert shard")
         line["ep_shard"] = ep_shard_line(dev, bench)
     if args.workload == "decode" and not args.no_backward:
+        progress("backward")
         line["backward"] = backward_line(workloads.workload("prefill"), dev, bench.w,
                                          args.backward_steps, bench.pw)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         n_cpu = args.cpu_tokens or (4 if cfg["w_dtype"] == "mxfp4" else 64)
+        progress(f"cpu baseline: the oracle on {min(n_cpu, cfg['T'])} tokens")
         line["cpu_baseline"] = cpu_baseline(cfg, bench, min(n_cpu, cfg["T"]))
     print(json.dumps(line), flush=True)
     return 0

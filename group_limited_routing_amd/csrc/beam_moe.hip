@@ -54,13 +54,16 @@ Layout make_layout(const Shape& s) {
     L.h = take(P * I * 2);   // bf16 SwiGLU output
   }
   L.y = take(P * H * 2);     // bf16 expert outputs, scaled by rsf * w
-  if (!s.x_f32) {
+  L.wsplit = L.zpart = 0;
+  L.router_ks = L.router_x3 = 0;
+  if (s.T <= kRouterSplitMaxT) {
+    L.router_ks = router_small_split(s.H);
+    L.zpart = take((size_t)L.router_ks * T * E * 4);
+  } else if (!s.x_f32) {
+    L.router_x3 = 1;
     L.router_ks = router_ksplit(s.T, s.H);
     L.wsplit = take(3 * E * H * 2);
     L.zpart = take((size_t)L.router_ks * T * E * 4);
-  } else {
-    L.router_ks = 0;
-    L.wsplit = L.zpart = 0;
   }
   L.total = off;
   return L;
@@ -250,16 +253,22 @@ Buffers carve(const Layout& L, void* ws) {
   return B;
 }
 
-// Router logits and selection. bf16 tokens: split weights, partial logits,
-// summed by the selection (which stores them when logits are requested).
-// fp32 tokens: fp32 MFMA logits straight into z.
+// Router logits and selection. Up to kRouterSplitMaxT tokens: fp32 MFMA
+// partial logits over several K ranges. More bf16 tokens: split weights,
+// partial logits on the bf16 matrix cores. Partials are summed by the
+// selection (which stores the sum when logits are requested). More fp32
+// tokens: fp32 MFMA logits straight into z.
 beam_status route_tokens(const Shape& s, const Layout& L, const Buffers& B, const void* x,
                          const float* router_w, const float* bias, float* logits_out,
                          int32_t* idx, float* w, hipStream_t st, float* s_sel = nullptr) {
   const int T = s.T;
   if (L.router_ks > 0) {
-    STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_x3((const uint16_t*)x, router_w, B.wsplit, B.zpart,
-                                                     T, s.H, L.router_ks, st));
+    if (L.router_x3)
+      STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_x3((const uint16_t*)x, router_w, B.wsplit,
+                                                       B.zpart, T, s.H, L.router_ks, st));
+    else
+      STAGE(BEAM_STAGE_ROUTER_LOGITS, launch_router_logits_split(x, s.x_f32, router_w, B.zpart, T,
+                                                                 s.H, L.router_ks, st));
     STAGE(BEAM_STAGE_SELECT, launch_select(B.zpart, L.router_ks, (size_t)T * s.E, logits_out, bias, T,
                                            s.n_group, s.topk_group, s.top_k, idx, w, s_sel, st));
   } else {

@@ -27,10 +27,15 @@ struct Shape {
 struct Layout {
   size_t z, idx, w, chist, cbase, counts, offsets, meta, tile_e, tile_r, e_tstart, e_ntiles;
   size_t stok, sw, inv, xq, xs, hamax, h, hq, hs, y, total;
-  size_t wsplit, zpart;  // bf16 tokens: split router weights, partial logits
+  size_t wsplit, zpart;  // split router weights (bf16 tokens, many), partial logits
   int nchunks, max_mtiles;
-  int router_ks;         // K ranges of the partial logits (0: fp32 router)
+  int router_ks;         // K ranges of the partial logits (0: logits straight into z)
+  int router_x3;         // 1: partials from the split-weight bf16 kernel, 0: fp32 kernel
 };
+
+// Up to this many tokens the router runs the fp32 kernel with its reduction
+// split over workgroups (partial logits summed by the selection).
+constexpr int kRouterSplitMaxT = 256;
 
 Layout make_layout(const Shape& s);
 bool use_stream_gemm(const Shape& s);
@@ -40,6 +45,11 @@ int mtile_bound(const Shape& s, int BM);
 
 hipError_t launch_router_logits(const void* x, int x_f32, const float* W, float* z, int T, int H,
                                 hipStream_t st);
+// Few tokens: partial logits zp[kz, t, e] over nz = router_small_split(H)
+// ranges of the hidden dimension, from the fp32 kernel.
+int router_small_split(int H);
+hipError_t launch_router_logits_split(const void* x, int x_f32, const float* W, float* zp, int T,
+                                      int H, int nz, hipStream_t st);
 // bf16 tokens: router weights split into three bf16 parts, partial logits
 // over router_ksplit(T, H) ranges of the hidden dimension.
 int router_ksplit(int T, int H);

@@ -24,7 +24,10 @@ namespace beam {
 // consumes element j of every lane, so the four MFMAs together cover the 16
 // k values. Each j keeps its own accumulator (shorter rounding chains); the
 // four are summed in a fixed order, and K splits are summed through LDS in
-// wave order, so the result does not depend on scheduling.
+// wave order, so the result does not depend on scheduling. With gridDim.z
+// = Z > 1 the reduction is also split over Z workgroups: workgroup z covers
+// the z-th of Z equal K ranges and writes its partial logits to
+// z + z * T * 256 (summed in z order by the selection).
 template <typename XT, int MW, int KS, int NB>
 __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x,
                                                             const float* __restrict__ W,
@@ -35,8 +38,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
   const int r = lane & 15, g = lane >> 4;
   const int tok0 = blockIdx.x * (16 * MW) + wm * 16;
   const int e0 = blockIdx.y * (16 * NB);
-  const int kper = H / KS;
-  const int kb = ks * kper;
+  const int kper = H / (KS * (int)gridDim.z);
+  const int kb = ((int)blockIdx.z * KS + ks) * kper;
+  z += (size_t)blockIdx.z * T * kExperts;
 
   const int tok = min(tok0 + r, T - 1);
   const XT* xrow = x + (size_t)tok * H + kb + 4 * g;
@@ -285,11 +289,21 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ z
 
   const size_t zo = (size_t)t * kExperts + 4 * lane;
   u32x4 zv = ld16(z + zo);
-  for (int p = 1; p < nparts; ++p) {
-    const u32x4 o = ld16(z + p * pstride + zo);
+  auto add = [&](const u32x4& o) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) zv[i] = __float_as_uint(__uint_as_float(zv[i]) + __uint_as_float(o[i]));
+  };
+  // partials 1, 2, ... added in order; loaded four at a time so that the
+  // loads of a batch are in flight together
+  int p = 1;
+  for (; p + 4 <= nparts; p += 4) {
+    u32x4 o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = ld16(z + (p + q) * pstride + zo);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) add(o[q]);
   }
+  for (; p < nparts; ++p) add(ld16(z + p * pstride + zo));
   if (zout) st16(zout + zo, zv);
   const u32x4 bv = ld16(bias + 4 * lane);
   float s[4], key[4];
@@ -377,6 +391,23 @@ hipError_t launch_router_logits(const void* x, int x_f32, const float* W, float*
     else
       router_logits_kernel<uint16_t, 4, 1, 4><<<grid, 256, 0, st>>>((const uint16_t*)x, W, z, T, H);
   }
+  return hipGetLastError();
+}
+
+int router_small_split(int H) {
+  // 16 k per MFMA step x 4 waves per split
+  return H % 512 == 0 ? 8 : H % 256 == 0 ? 4 : H % 128 == 0 ? 2 : 1;
+}
+
+hipError_t launch_router_logits_split(const void* x, int x_f32, const float* W, float* zp, int T,
+                                      int H, int nz, hipStream_t st) {
+  // Few tokens: 16x16 tiles, the reduction split over the 4 waves and over
+  // nz workgroups, so that enough workgroups stream the router matrix.
+  dim3 grid((T + 15) / 16, kExperts / 16, nz);
+  if (x_f32)
+    router_logits_kernel<float, 1, 4, 1><<<grid, 256, 0, st>>>((const float*)x, W, zp, T, H);
+  else
+    router_logits_kernel<uint16_t, 1, 4, 1><<<grid, 256, 0, st>>>((const uint16_t*)x, W, zp, T, H);
   return hipGetLastError();
 }
 

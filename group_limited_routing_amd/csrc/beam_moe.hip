@@ -410,11 +410,19 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
   const beam_status rs = route_tokens(s, L, B, x, router_w, expert_bias, router_logits_out, idx, w,
                                       st);
   if (rs != BEAM_OK) return rs;
-  STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(idx, T, k, B.chist, st));
-  STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts, B.offsets, B.meta,
-                               B.tile_e, B.tile_r, B.e_tstart, B.e_ntiles, expert_counts_out, st,
-                               e0, e1));
-  STAGE(BEAM_STAGE_PERM_SCATTER, launch_perm_scatter(idx, w, T, k, s.rsf, B.cbase, B.offsets, B.stok, B.sw, B.inv, st));
+  if (L.nchunks == 1) {
+    STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_single(idx, w, T, k, s.rsf, BM, B.counts, B.offsets,
+                                                   B.meta, B.tile_e, B.tile_r, B.e_tstart,
+                                                   B.e_ntiles, expert_counts_out, B.stok, B.sw,
+                                                   B.inv, st, e0, e1));
+  } else {
+    STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(idx, T, k, B.chist, st));
+    STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts,
+                                                 B.offsets, B.meta, B.tile_e, B.tile_r, B.e_tstart,
+                                                 B.e_ntiles, expert_counts_out, st, e0, e1));
+    STAGE(BEAM_STAGE_PERM_SCATTER, launch_perm_scatter(idx, w, T, k, s.rsf, B.cbase, B.offsets,
+                                                       B.stok, B.sw, B.inv, st));
+  }
 
   GemmArgs g{};
   g.tile_e = B.tile_e;
@@ -549,12 +557,19 @@ beam_status backward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
   const beam_status rs = route_tokens(s, L, B, x, router_w, expert_bias, nullptr, B.idx, B.w, st,
                                       ssel);
   if (rs != BEAM_OK) return rs;
-  STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(B.idx, T, k, B.chist, st));
-  STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts, B.offsets,
-                                               B.meta, B.tile_e, B.tile_r, B.e_tstart, B.e_ntiles,
-                                               nullptr, st));
-  STAGE(BEAM_STAGE_PERM_SCATTER, launch_perm_scatter(B.idx, B.w, T, k, s.rsf, B.cbase, B.offsets,
-                                                     B.stok, B.sw, B.inv, st));
+  if (L.nchunks == 1) {
+    STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_single(B.idx, B.w, T, k, s.rsf, BM, B.counts,
+                                                   B.offsets, B.meta, B.tile_e, B.tile_r,
+                                                   B.e_tstart, B.e_ntiles, nullptr, B.stok, B.sw,
+                                                   B.inv, st));
+  } else {
+    STAGE(BEAM_STAGE_PERM_HIST, launch_perm_hist(B.idx, T, k, B.chist, st));
+    STAGE(BEAM_STAGE_PERM_SCAN, launch_perm_scan(B.chist, L.nchunks, BM, B.cbase, B.counts,
+                                                 B.offsets, B.meta, B.tile_e, B.tile_r,
+                                                 B.e_tstart, B.e_ntiles, nullptr, st));
+    STAGE(BEAM_STAGE_PERM_SCATTER, launch_perm_scatter(B.idx, B.w, T, k, s.rsf, B.cbase,
+                                                       B.offsets, B.stok, B.sw, B.inv, st));
+  }
   if (wg) STAGE(BEAM_STAGE_BWD_TRANSPOSE, launch_segment_cols(B.counts, pcol, st));
 
   GemmArgs g{};

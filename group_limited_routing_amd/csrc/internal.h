@@ -68,6 +68,12 @@ hipError_t launch_perm_scan(const int32_t* chist, int nchunks, int BM, int32_t* 
 hipError_t launch_perm_scatter(const int32_t* idx, const float* w, int T, int k, float rsf,
                                const int32_t* cbase, const int32_t* offsets, int32_t* stok,
                                float* sw, int32_t* inv, hipStream_t st);
+// One chunk (T <= 256): hist, scan and scatter in one launch, same results.
+hipError_t launch_perm_single(const int32_t* idx, const float* w, int T, int k, float rsf, int BM,
+                              int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,
+                              int32_t* tile_r, int32_t* e_tstart, int32_t* e_ntiles,
+                              int32_t* counts_out, int32_t* stok, float* sw, int32_t* inv,
+                              hipStream_t st, int e0 = 0, int e1 = kExperts);
 
 struct GemmArgs {
   const void* a;            // gate/up: x [T, H]; down: h_perm [T*k, I]

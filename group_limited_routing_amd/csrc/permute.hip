@@ -197,6 +197,68 @@ hipError_t launch_combine_shard(const void* y, const int32_t* inv, const int32_t
   return hipGetLastError();
 }
 
+// One chunk (T <= 256): the histogram, both scans, the tile list and the
+// scatter of the three kernels above in one workgroup, with the same results
+// (the chunk's base per expert is 0).
+__global__ __launch_bounds__(256) void perm_single_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ w, int T, int k, float rsf, int BM,
+    int e0, int e1, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ meta, int32_t* __restrict__ tile_e, int32_t* __restrict__ tile_r,
+    int32_t* __restrict__ e_tstart, int32_t* __restrict__ e_ntiles, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ stok, float* __restrict__ sw, int32_t* __restrict__ inv) {
+  __shared__ uint32_t mask[kExperts * kMaskWords];
+  __shared__ int wsum[4];
+  __shared__ int eoff[kExperts];
+  build_masks(mask, idx, T, k, 0);
+  const int e = threadIdx.x;
+  int run = 0;
+#pragma unroll
+  for (int ww = 0; ww < kMaskWords; ++ww) run += __popc(mask[e * kMaskWords + ww]);
+  counts[e] = run;
+  if (counts_out) counts_out[e] = run;
+  const int off = block_exclusive_scan(run, wsum);
+  offsets[e] = off;
+  if (e == kExperts - 1) offsets[kExperts] = off + run;
+  const int mt = (e >= e0 && e < e1) ? (run + BM - 1) / BM : 0;
+  const int ts = block_exclusive_scan(mt, wsum);
+  e_tstart[e] = ts;
+  e_ntiles[e] = mt;
+  for (int i = 0; i < mt; ++i) {
+    tile_e[ts + i] = e;
+    tile_r[ts + i] = off + i * BM;
+  }
+  if (e == kExperts - 1) meta[0] = ts + mt;
+  eoff[e] = off;
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t >= T) return;
+  const int word = t >> 5;
+  const uint32_t below = (1u << (t & 31)) - 1u;
+  for (int j = 0; j < k; ++j) {
+    const size_t q = (size_t)t * k + j;
+    const int ex = idx[q];
+    int rank = 0;
+    for (int ww = 0; ww < word; ++ww) rank += __popc(mask[ex * kMaskWords + ww]);
+    rank += __popc(mask[ex * kMaskWords + word] & below);
+    const int pos = eoff[ex] + rank;
+    stok[pos] = t;
+    sw[pos] = rsf * w[q];
+    inv[q] = pos;
+  }
+}
+
+hipError_t launch_perm_single(const int32_t* idx, const float* w, int T, int k, float rsf, int BM,
+                              int32_t* counts, int32_t* offsets, int32_t* meta, int32_t* tile_e,
+                              int32_t* tile_r, int32_t* e_tstart, int32_t* e_ntiles,
+                              int32_t* counts_out, int32_t* stok, float* sw, int32_t* inv,
+                              hipStream_t st, int e0, int e1) {
+  if (T > kChunk) return hipErrorInvalidValue;
+  perm_single_kernel<<<1, 256, 0, st>>>(idx, w, T, k, rsf, BM, e0, e1, counts, offsets, meta,
+                                        tile_e, tile_r, e_tstart, e_ntiles, counts_out, stok, sw,
+                                        inv);
+  return hipGetLastError();
+}
+
 hipError_t launch_perm_scatter(const int32_t* idx, const float* w, int T, int k, float rsf,
                                const int32_t* cbase, const int32_t* offsets, int32_t* stok,
                                float* sw, int32_t* inv, hipStream_t st) {

@@ -264,12 +264,26 @@ void router_x3_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict
   }
 }
 
-// Best (key, index) of two candidates: larger key, equal keys to the lower
-// index; idx < 0 marks "no candidate".
-__device__ __forceinline__ void take_better(float& k, int& i, float ok, int oi) {
-  const bool other = (oi >= 0) && (i < 0 || ok > k || (ok == k && oi < i));
-  k = other ? ok : k;
-  i = other ? oi : i;
+// Maximum of v over the wave, in every lane. DPP steps: neighbours and
+// quads (quad permutes), 8 and 16 lanes (half-row and row mirrors), then
+// rows 0-1 and 0-3 through the row broadcasts of lanes 15 and 31; lane 63
+// ends with the maximum of all 64. A source lane outside the move keeps the
+// lane's own value (old = v), which leaves the maximum unchanged.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF,
+                                            false);
+  return fmaxf(v, __int_as_float(o));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = dpp_max<0xB1>(v);        // quad_perm [1, 0, 3, 2]
+  v = dpp_max<0x4E>(v);        // quad_perm [2, 3, 0, 1]
+  v = dpp_max<0x141>(v);       // row_half_mirror
+  v = dpp_max<0x140>(v);       // row_mirror
+  v = dpp_max<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // One wave per token. Lane l holds experts 4l..4l+3. A group of
@@ -333,36 +347,39 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ z
   const int grp = lane / lpg;
 
   // Rank of this lane's group; kept if fewer than topk_group groups beat it.
+  // Every lane of a group holds its score, so lane gg * lpg speaks for group gg.
   int rank = 0;
   for (int gg = 0; gg < n_group; ++gg) {
-    const float sc = __shfl(gscore, gg * lpg);
+    const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gscore), gg * lpg));
     rank += (sc > gscore || (sc == gscore && gg < grp)) ? 1 : 0;
   }
   uint32_t avail = (rank < topk_group) ? 0xFu : 0u;
 
-  // top_k rounds of a wave-wide argmax over the remaining candidates.
+  // top_k rounds: the largest remaining key (a wave max), then the lowest
+  // expert index holding it: the first lane whose remaining keys reach the
+  // max (lane l holds experts 4l .. 4l + 3), its first slot with that key.
   float sum = 0.f, my_s = 0.f;
   int my_i = 0;
   for (int j = 0; j < top_k; ++j) {
-    float bk = -INFINITY;
-    int bi = -1;
+    float lmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if ((avail >> i) & 1u) take_better(bk, bi, key[i], 4 * lane + i);
+      if ((avail >> i) & 1u) lmax = fmaxf(lmax, key[i]);
+    const float m = wave_max(lmax);
+    // at least top_k candidates exist, so some lane with candidates left holds m
+    const uint64_t hold = __ballot(avail != 0u && lmax == m);
+    const int owner = __ffsll((unsigned long long)hold) - 1;
+    int first = 3;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const int oi = __shfl_xor(bi, off);
-      take_better(bk, bi, ok, oi);
-    }
-    // bi is the same on every lane; at least top_k candidates exist, so bi >= 0.
-    const int owner = bi >> 2, slot = bi & 3;
+    for (int i = 3; i >= 0; --i)
+      if (((avail >> i) & 1u) && key[i] == m) first = i;
+    const int slot = __builtin_amdgcn_readlane(first, owner);
     if (lane == owner) avail &= ~(1u << slot);
     const float sv = (slot == 0) ? s[0] : (slot == 1) ? s[1] : (slot == 2) ? s[2] : s[3];
-    const float ws = __shfl(sv, owner);
+    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), owner));
     sum += ws;
     if (lane == j) {
-      my_i = bi;
+      my_i = 4 * owner + slot;
       my_s = ws;
     }
   }

@@ -362,7 +362,8 @@ typedef enum beam_stage {
   BEAM_STAGE_ROUTER_LOGITS = 0, /* fp32 router logits */
   BEAM_STAGE_SELECT = 1,        /* sigmoid, bias, group top-2, kept groups, top-k, normalise */
   BEAM_STAGE_PERM_HIST = 2,     /* per-chunk expert histogram */
-  BEAM_STAGE_PERM_SCAN = 3,     /* counts, offsets, GEMM tile list */
+  BEAM_STAGE_PERM_SCAN = 3,     /* counts, offsets, GEMM tile list (up to 256 tokens:
+                                   the whole permutation, one launch) */
   BEAM_STAGE_PERM_SCATTER = 4,  /* stable scatter into expert order */
   BEAM_STAGE_QUANT_X = 5,       /* fp8 weights only: per-token E4M3 quantisation of x */
   BEAM_STAGE_GATEUP = 6,        /* grouped gate/up GEMM + SwiGLU */

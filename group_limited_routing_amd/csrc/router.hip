@@ -54,8 +54,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[nb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k = 0; k < kper; k += 16) {
-    float a[4];
+  // One 16-k step: four k values of x per lane and of each of the NB weight rows.
+  auto load = [&](int k, float (&a)[4], u32x4 (&b)[NB]) {
     if constexpr (sizeof(XT) == 4) {
       u32x4 v = ld16(xrow + k);
 #pragma unroll
@@ -67,13 +67,34 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
       a[2] = bf16_bits_to_f32(v[1] & 0xffffu);
       a[3] = bf16_bits_to_f32(v[1] >> 16);
     }
-    u32x4 b[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) b[nb] = ld16(wrow[nb] + k);
+  };
+  auto step = [&](const float (&a)[4], const u32x4 (&b)[NB]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb][j] = mfma_f32(a[j], __uint_as_float(b[nb][j]), acc[nb][j]);
+  };
+  // U steps at a time, all their loads issued before their MFMAs, so that
+  // a short K range is not a chain of one load round trip per step; the
+  // order of the steps (and of the sums) is unchanged
+  constexpr int U = NB == 1 ? 8 : 2;
+  int k = 0;
+  for (; k + 16 * U <= kper; k += 16 * U) {
+    float a[U][4];
+    u32x4 b[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load(k + 16 * u, a[u], b[u]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) step(a[u], b[u]);
+  }
+  for (; k < kper; k += 16) {
+    float a[4];
+    u32x4 b[NB];
+    load(k, a, b);
+    step(a, b);
   }
 
   f32x4 res[NB];

@@ -156,9 +156,10 @@ def stored_traffic(workload, name="gateup", sources=KERNEL_SOURCES, key="hbm_byt
     if vals.get("kernel_source_sha") != kernel_source_sha(sources):
         return None
     try:
-        return int(float(vals[key]))
+        v = float(vals[key])
     except (KeyError, ValueError):
         return None
+    return int(v) if key == "hbm_bytes_per_launch" else v
 
 
 class Bench:
@@ -214,6 +215,17 @@ class Bench:
             s, g, k = self.residual
             self.gl.forward_residual(self.x, self.rw, self.b, w["w_gate"], w["w_up"],
                                      w["w_down"], s, g, k, **kw)
+
+    def routed_forward(self):
+        """One forward of the timed configuration that also returns its routing."""
+        w = self.pw
+        out, r = self.gl.forward(self.x, self.rw, self.b, w["w_gate"], w["w_up"], w["w_down"],
+                                 scales=self.scales, packed=True, n_group=self.cfg["n_group"],
+                                 topk_group=self.cfg["topk_group"], top_k=self.cfg["top_k"],
+                                 routed_scaling_factor=self.cfg["routed_scaling_factor"],
+                                 workspace=self.ws, return_routing=True)
+        self.torch.cuda.synchronize()
+        return out, r
 
     def run(self, steps, warmup):
         torch, gl = self.torch, self.gl
@@ -383,7 +395,9 @@ def ep_shard_line(dev, bench, gpus=8, steps=50):
 
 
 def cpu_baseline(cfg, bench, n_tokens):
-    """The oracle on the first n_tokens tokens of the same inputs (float64)."""
+    """The oracle on the first n_tokens tokens of the same inputs (float64),
+    timed; then the timed configuration's routing and outputs on those tokens
+    compared with the oracle's. Returns (baseline, parity)."""
     import numpy as np
     import torch
     import oracle
@@ -413,14 +427,36 @@ def cpu_baseline(cfg, bench, n_tokens):
         return tuple(host[e][k].double().numpy() for k in ("w_gate", "w_up", "w_down"))
 
     t0 = time.perf_counter()
-    oracle.forward_tokens(tok, bench.x.cpu().double().numpy(), rw64, b64, get,
-                          n_group=cfg["n_group"], topk_group=cfg["topk_group"], top_k=cfg["top_k"],
-                          routed_scaling_factor=cfg["routed_scaling_factor"], fp8=fp8 or mx)
+    ref, _ = oracle.forward_tokens(tok, bench.x.cpu().double().numpy(), rw64, b64, get,
+                                   n_group=cfg["n_group"], topk_group=cfg["topk_group"],
+                                   top_k=cfg["top_k"],
+                                   routed_scaling_factor=cfg["routed_scaling_factor"], fp8=fp8 or mx)
     dt = time.perf_counter() - t0
-    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s",
+    base = {"value": round(n_tokens / dt, 3), "unit": "tokens/s",
             "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"first {n_tokens} tokens of the {cfg['name']} workload ({len(need)} experts), "
                       f"float64 numpy, {dt:.1f} s"}
+    # the timed forward's routing and output on the same tokens against the
+    # oracle's: expert indices outside the near-tie band (margin < 1e-6) must
+    # agree, outputs are compared where the routing agrees
+    out, gr = bench.routed_forward()
+    gidx = gr["topk_idx"][:n_tokens].cpu().numpy().astype(np.int64)
+    near = r["margin"] < 1e-6
+    same = np.all(gidx == r["idx"], axis=1)
+    got = out[:n_tokens].cpu().double().numpy()[same]
+    want = ref[same]
+    d = got - want
+    row_inf = np.abs(want).max(axis=1)
+    parity = {"tokens": n_tokens,
+              "routing_mismatches": int(np.sum(~same & ~near)),
+              "near_ties": int(near.sum()),
+              "outputs_compared": int(same.sum()),
+              "max_rel": float(np.max(np.abs(d).max(axis=1) / np.where(row_inf > 0, row_inf, 1.0)))
+              if same.any() else None,
+              "normwise": float(np.linalg.norm(d) / max(np.linalg.norm(want), 1e-300))
+              if same.any() else None,
+              "bars": {"max_rel": 2e-2, "normwise": 5e-3}}
+    return base, parity
 
 
 def summarize(d):
@@ -453,6 +489,65 @@ def _counter_rows(d):
         with open(path) as f:
             rows += list(csv.DictReader(f))
     return rows
+
+
+MFMA_COUNTERS = "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CU_CYCLES"
+N_SIMDS = 1024  # 256 CUs x 4 SIMDs
+N_XCDS = 8      # GRBM_GUI_ACTIVE sums one count per XCD
+
+
+def write_mfma(pmc_dir, workload):
+    """Matrix-core utilisation of the two expert GEMM launches from one
+    rocprofv3 --pmc pass (MFMA_COUNTERS) over `bench.py --workload W`:
+    per kernel the mean dispatch duration, the shader clock (GRBM_GUI_ACTIVE
+    per XCD over the duration), the fraction of SIMD cycles the matrix core
+    was busy (SQ_VALU_MFMA_BUSY_CYCLES over SIMDs x cycles) and the MFMA
+    instructions per dispatch."""
+    import re
+    rows = _counter_rows(pmc_dir)
+    pat = re.compile(r"beam::gemm_\w+<([01]),")
+    per = {}
+    for r in rows:
+        m = pat.search(r["Kernel_Name"])
+        if not m:
+            continue
+        k = per.setdefault(m.group(1), {"name": r["Kernel_Name"], "ids": {}, "c": {}})
+        did = r["Dispatch_Id"]
+        if did not in k["ids"]:
+            k["ids"][did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        k["c"][r["Counter_Name"]] = k["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if "0" not in per:
+        raise SystemExit(f"no gate/up GEMM dispatches under {pmc_dir}")
+    lines = []
+    for mode, label in (("0", "gateup"), ("1", "down")):
+        if mode not in per:
+            continue
+        k = per[mode]
+        n = len(k["ids"])
+        dur = sum(k["ids"].values()) / n
+        c = {name: v / n for name, v in k["c"].items()}
+        cyc = c["GRBM_GUI_ACTIVE"] / N_XCDS
+        lines += [f"{label}_kernel = {k['name']}",
+                  f"{label}_dispatches = {n}",
+                  f"{label}_duration_ms = {dur * 1e3:.4f}",
+                  f"{label}_clock_ghz = {cyc / dur / 1e9:.3f}",
+                  f"{label}_mfma_busy = {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMDS * cyc):.4f}",
+                  f"{label}_mfma_insts = {c['SQ_INSTS_MFMA']:.0f}",
+                  f"{label}_cu_busy = {c['SQ_BUSY_CU_CYCLES'] / (256 * cyc):.4f}"]
+    cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {MFMA_COUNTERS} "
+           "--kernel-include-regex 'gemm' -d <dir> -o run --output-format csv "
+           f"-- python3 /root/repo/bench.py --workload {workload} --steps 3 --warmup 1 --no-prefill "
+           "--no-residual --no-backward --no-shard --no-cpu-baseline")
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}_counters.txt")
+    with open(path, "w") as fh:
+        fh.write(f"# Matrix-core utilisation of the expert GEMMs, workload {workload}, one MI355X\n")
+        fh.write(f"# command: {cmd}\n")
+        fh.write(f"#   python3 bench.py --mfma <dir> --workload {workload}\n")
+        fh.write("# clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES /\n")
+        fh.write("# (1024 SIMDs x clock cycles); cu_busy = SQ_BUSY_CU_CYCLES / (256 CUs x clock cycles)\n")
+        fh.write("\n".join(lines) + "\n")
+        fh.write(f"kernel_source_sha = {kernel_source_sha()}\n")
+    print(open(path).read())
 
 
 def write_wgrad_traffic(fetch_dir, write_dir):
@@ -561,6 +656,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--mfma", metavar="PMC_DIR")
     ap.add_argument("--wgrad-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
 
@@ -572,6 +668,9 @@ def main():
         return 0
     if args.wgrad_traffic:
         write_wgrad_traffic(args.wgrad_traffic[0], args.wgrad_traffic[1])
+        return 0
+    if args.mfma:
+        write_mfma(args.mfma, args.workload)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -612,13 +711,18 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4 x e4m3" if cfg["w_dtype"] == "mxfp4" else wdt,
         "data": "synthetic",
+        "device": {"name": torch.cuda.get_device_name(0),
+                   "arch": torch.cuda.get_device_properties(0).gcnArchName,
+                   "hip": torch.version.hip, "host_cores": len(os.sched_getaffinity(0))},
         "config": {"workload": describe(cfg), "T": cfg["T"], "hidden": cfg["hidden"],
                    "intermediate": cfg["intermediate"], "n_experts": cfg["n_experts"],
                    "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "top_k": cfg["top_k"],
                    "active_experts": bench.active, "max_over_mean_load": round(bench.max_over_mean, 4),
                    "parallelism": "single GPU"},
         "roofline": dict(rl, kernel=gateup_kernel(cfg), launch_ms=round(res["gateup_ms"], 4),
-                         algorithmic_bytes=gb, algorithmic_flops=gf),
+                         algorithmic_bytes=gb, algorithmic_flops=gf,
+                         mfma_busy=stored_traffic(cfg["name"], "mfma", key="gateup_mfma_busy"),
+                         clock_ghz=stored_traffic(cfg["name"], "mfma", key="gateup_clock_ghz")),
         "layer": {"pct_hbm": round(lb / step_s / 1e9 / HBM_PEAK_GBS, 4),
                   "pct_mfma": round(lf / step_s / 1e12 / MFMA_PEAK_TFLOPS[wdt], 4),
                   "algorithmic_bytes": lb, "flops": lf, "stages_ms": res["stages_ms"]},
@@ -649,7 +753,9 @@ def main():
             "max_over_mean_load": round(pb.max_over_mean, 4),
             "roofline": dict(roofline(pgb, pgf, pres["gateup_ms"] / 1e3, "bf16", stored_traffic("prefill")),
                              kernel=gateup_kernel(pcfg), launch_ms=round(pres["gateup_ms"], 4),
-                             algorithmic_bytes=pgb, algorithmic_flops=pgf),
+                             algorithmic_bytes=pgb, algorithmic_flops=pgf,
+                             mfma_busy=stored_traffic("prefill", "mfma", key="gateup_mfma_busy"),
+                             clock_ghz=stored_traffic("prefill", "mfma", key="gateup_clock_ghz")),
             "layer": {"pct_hbm": round(plb / ps / 1e9 / HBM_PEAK_GBS, 4),
                       "pct_mfma": round(plf / ps / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
                       "stages_ms": pres["stages_ms"]},
@@ -666,7 +772,7 @@ def main():
     if not args.no_cpu_baseline:
         n_cpu = args.cpu_tokens or (4 if cfg["w_dtype"] == "mxfp4" else 64)
         progress(f"cpu baseline: the oracle on {min(n_cpu, cfg['T'])} tokens")
-        line["cpu_baseline"] = cpu_baseline(cfg, bench, min(n_cpu, cfg["T"]))
+        line["cpu_baseline"], line["parity_sample"] = cpu_baseline(cfg, bench, min(n_cpu, cfg["T"]))
     print(json.dumps(line), flush=True)
     return 0
 

@@ -140,10 +140,10 @@ def roofline(bytes_, flops, seconds, wdt, traffic=None):
             "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS[wdt], 4), "traffic": traffic}
 
 
-def stored_traffic(workload, name="gateup", sources=KERNEL_SOURCES, key="hbm_bytes_per_launch"):
-    """HBM bytes per gate/up launch (or another stored figure) from the
-    committed counter summary, or None (missing, or counters taken on other
-    kernel sources)."""
+def stored_figure(workload, name="gateup", sources=KERNEL_SOURCES, key="hbm_bytes_per_launch"):
+    """A figure from a committed counter summary profiles/<name>_<workload>_counters.txt
+    (by default the HBM bytes per gate/up launch), or None: missing, or the
+    counters were taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"{name}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
@@ -336,7 +336,7 @@ def backward_line(cfg, dev, weights, steps, packed=None):
     by, fl = work[name]
     traffic = None
     if name == "bwd_wgrad":
-        traffic = stored_traffic("backward", "wgrad", WGRAD_SOURCES, "hbm_bytes_per_step")
+        traffic = stored_figure("backward", "wgrad", WGRAD_SOURCES, "hbm_bytes_per_step")
     rl = roofline(by, fl, per_step[name] / 1e3, "bf16", traffic)
     out = {"workload": f"backward of {describe(cfg)}; gradients of x, the router and all "
                        "expert weights (bf16), output gradient N(0, 1)",
@@ -695,7 +695,7 @@ def main():
     res = bench.run(args.steps, args.warmup)
     wdt = "fp8" if cfg["w_dtype"] in ("fp8", "mxfp4") else "bf16"
     gb, gf = gateup_work(cfg, bench.active)
-    rl = roofline(gb, gf, res["gateup_ms"] / 1e3, wdt, stored_traffic(cfg["name"]))
+    rl = roofline(gb, gf, res["gateup_ms"] / 1e3, wdt, stored_figure(cfg["name"]))
     lb, lf = layer_work(cfg, bench.active)
     step_s = res["ms_per_step"] / 1e3
     line = {
@@ -721,8 +721,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": dict(rl, kernel=gateup_kernel(cfg), launch_ms=round(res["gateup_ms"], 4),
                          algorithmic_bytes=gb, algorithmic_flops=gf,
-                         mfma_busy=stored_traffic(cfg["name"], "mfma", key="gateup_mfma_busy"),
-                         clock_ghz=stored_traffic(cfg["name"], "mfma", key="gateup_clock_ghz")),
+                         mfma_busy=stored_figure(cfg["name"], "mfma", key="gateup_mfma_busy"),
+                         clock_ghz=stored_figure(cfg["name"], "mfma", key="gateup_clock_ghz")),
         "layer": {"pct_hbm": round(lb / step_s / 1e9 / HBM_PEAK_GBS, 4),
                   "pct_mfma": round(lf / step_s / 1e12 / MFMA_PEAK_TFLOPS[wdt], 4),
                   "algorithmic_bytes": lb, "flops": lf, "stages_ms": res["stages_ms"]},
@@ -751,11 +751,11 @@ def main():
             "workload": describe(pcfg), "value": round(pcfg["T"] / ps, 1), "unit": "tokens/s",
             "ms_per_step": round(pres["ms_per_step"], 4), "steps": args.prefill_steps,
             "max_over_mean_load": round(pb.max_over_mean, 4),
-            "roofline": dict(roofline(pgb, pgf, pres["gateup_ms"] / 1e3, "bf16", stored_traffic("prefill")),
+            "roofline": dict(roofline(pgb, pgf, pres["gateup_ms"] / 1e3, "bf16", stored_figure("prefill")),
                              kernel=gateup_kernel(pcfg), launch_ms=round(pres["gateup_ms"], 4),
                              algorithmic_bytes=pgb, algorithmic_flops=pgf,
-                             mfma_busy=stored_traffic("prefill", "mfma", key="gateup_mfma_busy"),
-                             clock_ghz=stored_traffic("prefill", "mfma", key="gateup_clock_ghz")),
+                             mfma_busy=stored_figure("prefill", "mfma", key="gateup_mfma_busy"),
+                             clock_ghz=stored_figure("prefill", "mfma", key="gateup_clock_ghz")),
             "layer": {"pct_hbm": round(plb / ps / 1e9 / HBM_PEAK_GBS, 4),
                       "pct_mfma": round(plf / ps / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
                       "stages_ms": pres["stages_ms"]},

@@ -84,10 +84,10 @@ def test_traffic_summary_scales_by_the_copy(sandbox, monkeypatch):
                                     (2, GATEUP, "WRITE_SIZE", 1000, 0, 1),
                                     (3, GATEUP, "WRITE_SIZE", 1000, 0, 1)])
     bench.write_traffic(str(sandbox / "f"), str(sandbox / "w"), "decode")
-    assert bench.stored_traffic("decode") == (3000 * 2 + 1000) * 1024
+    assert bench.stored_figure("decode") == (3000 * 2 + 1000) * 1024
     # counters taken on other kernel sources are not used
     monkeypatch.setattr(bench, "kernel_source_sha", lambda paths=None: "fedcba9876543210")
-    assert bench.stored_traffic("decode") is None
+    assert bench.stored_figure("decode") is None
 
 
 def test_mfma_summary(sandbox):
@@ -102,11 +102,11 @@ def test_mfma_summary(sandbox):
             rows.append((d, kern, name, v, t0, t0 + 1_000_000))
     _write_counters(sandbox / "m", rows)
     bench.write_mfma(str(sandbox / "m"), "skewed")
-    assert bench.stored_traffic("skewed", "mfma", key="gateup_mfma_busy") == pytest.approx(0.5)
-    assert bench.stored_traffic("skewed", "mfma", key="gateup_clock_ghz") == pytest.approx(2.0)
-    assert bench.stored_traffic("skewed", "mfma", key="down_mfma_busy") == pytest.approx(0.25)
-    assert bench.stored_traffic("skewed", "mfma", key="gateup_cu_busy") == pytest.approx(0.9)
-    assert bench.stored_traffic("skewed", "mfma", key="gateup_mfma_insts") == 1000
+    assert bench.stored_figure("skewed", "mfma", key="gateup_mfma_busy") == pytest.approx(0.5)
+    assert bench.stored_figure("skewed", "mfma", key="gateup_clock_ghz") == pytest.approx(2.0)
+    assert bench.stored_figure("skewed", "mfma", key="down_mfma_busy") == pytest.approx(0.25)
+    assert bench.stored_figure("skewed", "mfma", key="gateup_cu_busy") == pytest.approx(0.9)
+    assert bench.stored_figure("skewed", "mfma", key="gateup_mfma_insts") == 1000
 
 
 def test_more_than_one_gpu_is_refused():

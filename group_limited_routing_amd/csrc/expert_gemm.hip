@@ -718,6 +718,26 @@ __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const Til
 // A slice is shared by 8 of them and each weight slice by 4 in the XCD's L2.
 constexpr int kGroupM = 4;
 
+// Tiles per XCD chunk in xcd_chunked_tile.
+constexpr int kXcdChunk = 32;
+
+// Tile taken by workgroup b of a grouped GEMM over n_tiles numbered tiles.
+// Workgroups go to the 8 XCDs round-robin (b % 8). Chunks of kXcdChunk
+// consecutive tiles are dealt to the XCDs in turn: the blocks running
+// together on one XCD (32 CUs) take one chunk and share its operands in that
+// XCD's L2, and the 8 XCDs together work on 256 consecutive tiles. So one
+// expert's tiles run on the whole chip at once, and its weights and rows
+// (about 160 MB for an expert of 10K rows) stay in the 256 MB MALL between
+// its M-tile groups; a contiguous share per XCD would run eight experts at
+// once, whose re-reads would miss the MALL. Tiles of the last, partial round
+// of 256 go round-robin.
+__device__ __forceinline__ int xcd_chunked_tile(int b, int n_tiles) {
+  constexpr int R = 8 * kXcdChunk;
+  if (b >= n_tiles / R * R) return b;
+  const int q = b >> 3;  // the block's place on its XCD
+  return ((q / kXcdChunk) * 8 + (b & 7)) * kXcdChunk + q % kXcdChunk;
+}
+
 // ---------------------------------------------------------------- wide variant
 // Prefill with packed weights. A workgroup of 8 waves (two per SIMD) computes
 // BM rows x 256 weight rows (gate/up: 128 gate + 128 up columns; down: 256
@@ -729,10 +749,9 @@ constexpr int kGroupM = 4;
 // covers the LDS latency.
 //
 // Tile order: the active (M-tile, N-tile) pairs are numbered expert by
-// expert, in blocks of kGroupM M-tiles, N-tile-major inside a block; block b
-// takes number start(b % 8) + b / 8, where XCD x = b % 8 owns a contiguous
-// share, so blocks running together on one XCD share A and weight slices in
-// that XCD's L2.
+// expert, in blocks of kGroupM M-tiles, N-tile-major inside a block, and
+// dealt to the XCDs in chunks (xcd_chunked_tile), so blocks running together
+// on one XCD share A and weight slices in that XCD's L2.
 //
 // The MFMAs compute the transposed tile (weight fragment as the A operand):
 // each lane then holds 4 consecutive output columns of one row, stored as
@@ -753,9 +772,7 @@ void gemm_wide_kernel(GemmArgs p) {
   const int n_tiles = p.meta[0] * ntn;
   const int b = blockIdx.x;
   if (b >= n_tiles) return;
-  // XCD-contiguous numbering of the active tiles
-  const int xcd = b & 7, per = n_tiles >> 3, extra = n_tiles & 7;
-  const int j = xcd * per + min(xcd, extra) + (b >> 3);
+  const int j = xcd_chunked_tile(b, n_tiles);
   const int e = p.tile_e[j / ntn];
   const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
   const int jj = j - ts * ntn;
@@ -939,8 +956,7 @@ void gemm_dma_kernel(GemmArgs p) {
   const int n_tiles = p.meta[0] * ntn;
   const int b = blockIdx.x;
   if (b >= n_tiles) return;
-  const int xcd = b & 7, per = n_tiles >> 3, extra = n_tiles & 7;
-  const int j = xcd * per + min(xcd, extra) + (b >> 3);
+  const int j = xcd_chunked_tile(b, n_tiles);
   const int e = p.tile_e[j / ntn];
   const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
   const int jj = j - ts * ntn;
@@ -1268,8 +1284,7 @@ void gemm_dma8_kernel(GemmArgs p) {
   const int n_tiles = p.meta[0] * ntn;
   const int b = blockIdx.x;
   if (b >= n_tiles) return;
-  const int xcd = b & 7, per = n_tiles >> 3, extra = n_tiles & 7;
-  const int j = xcd * per + min(xcd, extra) + (b >> 3);
+  const int j = xcd_chunked_tile(b, n_tiles);
   const int e = p.tile_e[j / ntn];
   const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
   const int jj = j - ts * ntn;
@@ -1435,8 +1450,7 @@ void gemm_dma4_kernel(GemmArgs p) {
   const int n_tiles = p.meta[0] * ntn;
   const int b = blockIdx.x;
   if (b >= n_tiles) return;
-  const int xcd = b & 7, per = n_tiles >> 3, extra = n_tiles & 7;
-  const int j = xcd * per + min(xcd, extra) + (b >> 3);
+  const int j = xcd_chunked_tile(b, n_tiles);
   const int e = p.tile_e[j / ntn];
   const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
   const int jj = j - ts * ntn;

@@ -138,6 +138,15 @@ def test_fp8_dma_variant_256_rows():
     _full_compare("fp8 dma 256", cfg, 16, True)
 
 
+@pytest.mark.parametrize("T", [255, 256, 257, 512])
+def test_routing_paths_at_the_single_chunk_boundary(T):
+    # up to 256 tokens: split-K fp32 router logits and the one-launch
+    # permutation; from 257: the split-weight bf16 router and per-chunk
+    # histogram, scan and scatter
+    cfg = _case(T, 512, 256)
+    _full_compare(f"boundary T={T}", cfg, 23, True)
+
+
 def test_mxfp4_stream_variant():
     cfg = _case(200, 512, 1024, w_dtype="mxfp4")   # ragged M-tiles, 4-bit weights
     _full_compare("mxfp4 stream", cfg, 18, True)

@@ -222,6 +222,32 @@ def test_all_keys_equal_tie_rule():
     assert cnt[:8].tolist() == [50] * 8 and cnt[8:].sum() == 0
 
 
+@pytest.mark.parametrize("T", [64, 300])
+@pytest.mark.parametrize("dup", ["same_lane", "next_lane", "other_group"])
+def test_exact_ties_go_to_the_lower_index(T, dup):
+    """Experts with identical router rows and biases have identical keys, on
+    the GPU as in the oracle: pairs inside one lane's four experts (2i, 2i+1),
+    in neighbouring lanes of a group (8g + i, 8g + 4 + i), or in different
+    groups (e, e + 128, which also ties the group scores). Every tie goes to
+    the lower index, so the GPU's experts equal the oracle's on every token.
+    The seed leaves no near tie between different keys."""
+    dev = _dev()
+    cfg = _case(T, 256, 128)
+    x, rw, b, w = _inputs(cfg, 24, dev)
+    e = torch.arange(256, device=dev)
+    src = {"same_lane": e // 2, "next_lane": (e // 8) * 4 + e % 4, "other_group": e % 128}[dup]
+    rw = rw[src].contiguous()
+    b = b[src].contiguous()
+    out, r = run_forward(x, rw, b, w, cfg)
+    ora = oracle.route(x.cpu().double().numpy(), rw.cpu().double().numpy(),
+                       b.cpu().double().numpy(), cfg["n_group"], cfg["topk_group"], cfg["top_k"])
+    idx = r["topk_idx"].cpu().numpy()
+    assert np.array_equal(idx, ora["idx"])
+    np.testing.assert_allclose(r["topk_w"].cpu().numpy(), ora["w"], rtol=1e-5, atol=1e-6)
+    # the ties are real: some token chose both members of a duplicated pair
+    assert any(len(set(src[torch.as_tensor(row, device=dev)].tolist())) < 8 for row in idx)
+
+
 def test_route_entry_point_matches_forward():
     dev = _dev()
     cfg = _case(333, 512, 128)

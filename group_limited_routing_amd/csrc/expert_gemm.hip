@@ -1375,20 +1375,31 @@ void gemm_dma8_kernel(GemmArgs p) {
         if (hs & 1) {
           const uint8_t* st = smem + ((hs - 1 + half) % NS) * STAGE;
           Op32 af[NF], bfr[FN];
+          auto read_a = [&](int i) {
+            af[i].lo = ld16(st + aoff[i]);
+            af[i].hi = ld16(st + (aoff[i] ^ 16));
+          };
 #pragma unroll
           for (int f = 0; f < FN; ++f) {
             bfr[f].lo = ld16(st + boff[f]);
             bfr[f].hi = ld16(st + boff[f] + 16);
           }
+          read_a(0);
+          // A fragment i + 1 is read while the MFMAs of fragment i execute
 #pragma unroll
           for (int i = 0; i < NF; ++i) {
-            af[i].lo = ld16(st + aoff[i]);
-            af[i].hi = ld16(st + (aoff[i] ^ 16));
-          }
-#pragma unroll
-          for (int i = 0; i < NF; ++i)
 #pragma unroll
             for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_op(bfr[jn], af[i], acc[i][jn]);
+            if (i + 1 < NF) {
+              read_a(i + 1);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, FN - 2, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
         }
       }
       wait_lgkmcnt0();
@@ -1573,17 +1584,30 @@ void gemm_dma4_kernel(GemmArgs p) {
             }
             bsc[f] = (int)((*reinterpret_cast<const uint32_t*>(sc + soff[f]) >> (8 * (s & 3))) & 0xffu);
           }
+          // A fragment i + 1 is read while the MFMAs of fragment i execute
+          u32x4 alo[NF], ahi[NF];
+          alo[0] = ld16(st0 + aoff[0]);
+          ahi[0] = ld16(st1 + aoff[0]);
 #pragma unroll
           for (int i = 0; i < NF; ++i) {
-            const u32x4 lo = ld16(st0 + aoff[i]), hi = ld16(st1 + aoff[i]);
             i32x8 a;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              a[q] = (int)lo[q];
-              a[4 + q] = (int)hi[q];
+              a[q] = (int)alo[i][q];
+              a[4 + q] = (int)ahi[i][q];
             }
 #pragma unroll
             for (int jn = 0; jn < FN; ++jn) acc[i][jn] = mfma_fp4_fp8(bfr[jn], a, bsc[jn], acc[i][jn]);
+            if (i + 1 < NF) {
+              alo[i + 1] = ld16(st0 + aoff[i + 1]);
+              ahi[i + 1] = ld16(st1 + aoff[i + 1]);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, FN - 2, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }

@@ -9,23 +9,38 @@ load time by beam_moe_pack_weights:
 router logits, group-limited selection, permutation, both grouped expert
 GEMMs and the combine. Inputs and the 20 GB of expert weights are resident
 in HBM before the timed region. The default workload is Beam's decode shape
-(T = 64 tokens, hidden 5120, 256 experts x SwiGLU 2560, bf16 weights); a
-second measurement at the prefill shape (T = 4096) is reported in the same
-line under "prefill".
+(T = 64 tokens, hidden 5120, 256 experts x SwiGLU 2560, bf16 weights); the
+same line carries the prefill shape (T = 4096, balanced routing) under
+"prefill", the skewed routing (T = 16384, +0.5 bias on 8 experts) under
+"skewed" and the fp8 experts (T = 8192) under "fp8", each measured the
+same way.
+
+Timing: W untimed warm-up steps, then K steps back to back between two
+synchronisations, each bracketed by a pair of HIP events on the stream the
+library launches on. ms_per_step is the median of the K per-step times
+(ms_per_step_mean: the K steps' total over K). Kernel launch times come
+from separate passes in which the library records events around its
+launches, so the timed steps carry no per-kernel events.
 
 Printed fields beyond the usual ones:
-* roofline: the dominant kernel (the gate/up grouped GEMM), timed with HIP
-  events recorded by the library around its launches during the timed
-  region. achieved = algorithmic bytes (or flops) per launch / average
-  launch time; bytes = weights of the active experts + the x rows read + the
-  h rows written; flops = 4 * (T * top_k) * hidden * intermediate. The
-  bound is whichever of HBM (8 TB/s) and dense MFMA (bf16 2.5 PFLOP/s, fp8
-  5.0 PFLOP/s) takes longer for those figures. traffic: HBM bytes per
-  launch from the committed rocprofv3 counter summary for this kernel and
+* roofline: the dominant kernel (the gate/up grouped GEMM); achieved =
+  algorithmic bytes (or flops) per launch / average launch time. Bytes are
+  the method's own: the gate and up weights of the active experts and the
+  token rows the launch reads (x, or its E4M3 codes with quantised
+  weights); flops = 4 * (T * top_k) * hidden * intermediate. The bound is
+  whichever of HBM (8 TB/s) and dense MFMA (bf16 2.5 PFLOP/s, fp8 5.0
+  PFLOP/s) takes longer for those figures. traffic: HBM bytes per launch
+  from the committed rocprofv3 counter summary for this kernel and
   workload, scaled by the copy-kernel calibration stored with it; null when
   the summary is missing or was taken from other kernel sources.
+  down_roofline: the same for the down GEMM (its weights of the active
+  experts).
+* layer: the whole step against the block's algorithmic bytes (weights of
+  the active experts, x, out, the router weights) and flops;
+  design_overhead_bytes lists what the implementation moves beyond them
+  (the h and y round trips between the kernels, the E4M3 codes of x and h).
 * cpu_baseline: the oracle (numpy float64) on a bounded sample of the same
-  workload, on this machine's host cores.
+  workload, on this machine's host cores, median of 3 runs.
 
 Other modes: --workload tiny|decode|prefill|skewed|fp8 picks the timed
 workload; --calibrate-copy runs one plain device copy of 1 GiB before the
@@ -41,6 +56,7 @@ import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -103,18 +119,51 @@ def describe(cfg):
             f"({cfg['n_group']} groups, keep {cfg['topk_group']}), scale {cfg['routed_scaling_factor']}")
 
 
+# Bytes per element of the intermediate h as the gate/up launch stores it
+# for the down launch (bf16 weights: bf16 h; quantised weights: fp32 h, then
+# one E4M3 code per element).
+H_STORE_BYTES = {"bf16": 2, "fp8": 4, "mxfp4": 4}
+
+
+def quantised(cfg):
+    return cfg["w_dtype"] in ("fp8", "mxfp4")
+
+
 def gateup_work(cfg, active):
-    """Algorithmic bytes and flops of one gate/up launch."""
+    """Algorithmic bytes and flops of one gate/up launch: the gate and up
+    weights of the active experts and the token rows read (x, or its E4M3
+    codes with quantised weights). The h rows it writes for the down pass
+    are design overhead (design_overhead)."""
     T, H, I, k = cfg["T"], cfg["hidden"], cfg["intermediate"], cfg["top_k"]
     wb = WEIGHT_BYTES[cfg["w_dtype"]]
     xb = 4 if cfg["x_dtype"] == "f32" else 2
-    if cfg["w_dtype"] in ("fp8", "mxfp4"):
-        x_read, h_write = T * H * 1, T * k * I * 4   # e4m3 x codes in, fp32 h out
-    else:
-        x_read, h_write = T * H * xb, T * k * I * 2
-    bytes_ = int(active * 2 * I * H * wb) + x_read + h_write
+    x_read = T * H * (1 if quantised(cfg) else xb)
+    bytes_ = int(active * 2 * I * H * wb) + x_read
     flops = 4.0 * T * k * H * I
     return bytes_, flops
+
+
+def down_work(cfg, active):
+    """Algorithmic bytes and flops of one down launch: the down weights of
+    the active experts (its h input and y output are design overhead)."""
+    T, H, I, k = cfg["T"], cfg["hidden"], cfg["intermediate"], cfg["top_k"]
+    return int(active * I * H * WEIGHT_BYTES[cfg["w_dtype"]]), 2.0 * T * k * H * I
+
+
+def design_overhead(cfg):
+    """Bytes the implementation moves beyond the block's algorithmic ones:
+    h written by the gate/up launch and read back, y (the scaled expert
+    outputs, bf16) written by the down launch and read by the combine; with
+    quantised weights also the E4M3 codes of x and of h (written, read)."""
+    T, H, I, k = cfg["T"], cfg["hidden"], cfg["intermediate"], cfg["top_k"]
+    P = T * k
+    hb = H_STORE_BYTES[cfg["w_dtype"]]
+    out = {"h_round_trip": 2 * P * I * hb, "y_round_trip": 2 * P * H * 2}
+    if quantised(cfg):
+        out["x_codes"] = 2 * T * H
+        out["h_codes"] = 2 * P * I
+    out["total"] = sum(out.values())
+    return out
 
 
 def layer_work(cfg, active):
@@ -231,27 +280,41 @@ class Bench:
         torch, gl = self.torch, self.gl
         for _ in range(warmup):
             self.step()
-        torch.cuda.synchronize()
-        gl.profile_begin(["gateup"])
-        t0 = time.perf_counter()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
+        per, total, wall = timed_steps(torch, self.step, steps)
+        # the two GEMM launches, in a separate pass with the library's events
+        # around them (the timed steps above carry none)
+        gl.profile_begin(["gateup", "down"])
         for _ in range(steps):
             self.step()
-        e1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         prof = gl.profile_end()
-        ms_step = e0.elapsed_time(e1) / steps
-        gu_ms, gu_n = prof["gateup"]
-        # per-stage breakdown from a short separate pass (events on every stage)
+        # per-stage breakdown from a short pass with events on every stage
         gl.profile_begin()
         for _ in range(min(steps, 10)):
             self.step()
         torch.cuda.synchronize()
         stages = {k: round(v[0] / v[1], 4) for k, v in gl.profile_end().items()}
-        return {"ms_per_step": ms_step, "wall_s": wall, "gateup_ms": gu_ms / gu_n, "stages_ms": stages}
+        return {"ms_per_step": statistics.median(per), "ms_per_step_mean": total / steps,
+                "wall_s": wall, "gateup_ms": prof["gateup"][0] / prof["gateup"][1],
+                "down_ms": prof["down"][0] / prof["down"][1], "stages_ms": stages}
+
+
+def timed_steps(torch, step, steps):
+    """Run `steps` steps back to back between two synchronisations, each
+    bracketed by HIP events on the current stream (where the library
+    launches). Returns (per-step ms list, total ms, wall seconds)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    return per, ev[0][0].elapsed_time(ev[-1][1]), wall
 
 
 def backward_work(cfg, active):
@@ -309,15 +372,8 @@ class BackwardBench:
         torch, gl = self.torch, self.gl
         for _ in range(warmup):
             self.step()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            self.step()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        per, _, _ = timed_steps(torch, self.step, steps)
+        ms = statistics.median(per)
         gl.profile_begin()
         for _ in range(min(steps, 5)):
             self.step()
@@ -373,19 +429,16 @@ def ep_shard_line(dev, bench, gpus=8, steps=50):
                          out=out, workspace=ws)
     for _ in range(5):
         step()
-    torch.cuda.synchronize()
+    per, _, _ = timed_steps(torch, step, steps)
+    ms = statistics.median(per)
     gl.profile_begin(["gateup"])
-    e0_, e1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0_.record()
     for _ in range(steps):
         step()
-    e1_.record()
     torch.cuda.synchronize()
     prof = gl.profile_end()
-    ms = e0_.elapsed_time(e1_) / steps
     gu_ms = prof["gateup"][0] / prof["gateup"][1]
     H, I = cfg["hidden"], cfg["intermediate"]
-    gb = active * 2 * I * H * 2 + pairs * (H + I) * 2
+    gb = active * 2 * I * H * 2 + cfg["T"] * H * 2
     return {"workload": f"expert shard 0-{e1 - 1} of {gpus} at decode: {cfg['T']} tokens "
                         f"({gpus} x 64) routed over all experts, this shard's {pairs} pairs "
                         f"on {active} active experts, bf16 weights (its {e1} experts only)",
@@ -394,10 +447,20 @@ def ep_shard_line(dev, bench, gpus=8, steps=50):
                              kernel="gate/up", launch_ms=round(gu_ms, 4), algorithmic_bytes=gb)}
 
 
-def cpu_baseline(cfg, bench, n_tokens):
+def blas_threads():
+    """Threads of the BLAS library numpy calls (0 if it cannot be told)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
+    except Exception:  # threadpoolctl missing or unable to inspect the library
+        return 0
+
+
+def cpu_baseline(cfg, bench, n_tokens, runs=3):
     """The oracle on the first n_tokens tokens of the same inputs (float64),
-    timed; then the timed configuration's routing and outputs on those tokens
-    compared with the oracle's. Returns (baseline, parity)."""
+    timed `runs` times (the median is reported); then the timed
+    configuration's routing and outputs on those tokens compared with the
+    oracle's. Returns (baseline, parity)."""
     import numpy as np
     import torch
     import oracle
@@ -426,16 +489,22 @@ def cpu_baseline(cfg, bench, n_tokens):
                          for k in ("w_gate", "w_up", "w_down"))
         return tuple(host[e][k].double().numpy() for k in ("w_gate", "w_up", "w_down"))
 
-    t0 = time.perf_counter()
-    ref, _ = oracle.forward_tokens(tok, bench.x.cpu().double().numpy(), rw64, b64, get,
-                                   n_group=cfg["n_group"], topk_group=cfg["topk_group"],
-                                   top_k=cfg["top_k"],
-                                   routed_scaling_factor=cfg["routed_scaling_factor"], fp8=fp8 or mx)
-    dt = time.perf_counter() - t0
+    times = []
+    xall = bench.x.cpu().double().numpy()
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        ref, _ = oracle.forward_tokens(tok, xall, rw64, b64, get, n_group=cfg["n_group"],
+                                       topk_group=cfg["topk_group"], top_k=cfg["top_k"],
+                                       routed_scaling_factor=cfg["routed_scaling_factor"],
+                                       fp8=fp8 or mx)
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
     base = {"value": round(n_tokens / dt, 3), "unit": "tokens/s",
             "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "blas_threads": blas_threads(),
             "sample": f"first {n_tokens} tokens of the {cfg['name']} workload ({len(need)} experts), "
-                      f"float64 numpy, {dt:.1f} s"}
+                      f"float64 numpy, median of {runs} runs: {dt:.1f} s "
+                      f"(runs {', '.join(f'{t:.1f}' for t in times)} s)"}
     # the timed forward's routing and output on the same tokens against the
     # oracle's: expert indices outside the near-tie band (margin < 1e-6) must
     # agree, outputs are compared where the routing agrees
@@ -537,7 +606,7 @@ def write_mfma(pmc_dir, workload):
     cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {MFMA_COUNTERS} "
            "--kernel-include-regex 'gemm' -d <dir> -o run --output-format csv "
            f"-- python3 /root/repo/bench.py --workload {workload} --steps 3 --warmup 1 --no-prefill "
-           "--no-residual --no-backward --no-shard --no-cpu-baseline")
+           "--no-residual --no-backward --no-shard --no-fp8 --no-cpu-baseline")
     path = os.path.join(ROOT, "profiles", f"mfma_{workload}_counters.txt")
     with open(path, "w") as fh:
         fh.write(f"# Matrix-core utilisation of the expert GEMMs, workload {workload}, one MI355X\n")
@@ -612,7 +681,7 @@ def write_traffic(fetch_dir, write_dir, workload):
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --kernel-include-regex 'gemm|copyBuffer' "
            "-d <dir> -o run --output-format csv "
            f"-- python3 /root/repo/bench.py --workload {workload} --steps 3 --warmup 1 --no-prefill "
-           "--no-residual --no-backward --no-shard --no-cpu-baseline --calibrate-copy")
+           "--no-residual --no-backward --no-shard --no-fp8 --no-cpu-baseline --calibrate-copy")
     path = os.path.join(ROOT, "profiles", f"gateup_{workload}_counters.txt")
     with open(path, "w") as fh:
         fh.write(f"# HBM traffic of the gate/up grouped GEMM, workload {workload}, one MI355X\n")
@@ -634,6 +703,43 @@ def write_traffic(fetch_dir, write_dir, workload):
     print(open(path).read())
 
 
+def workload_line(cfg, bench, steps, warmup):
+    """Time one workload (Bench.run) and report it: throughput, the gate/up
+    and down launches against their rooflines, the whole layer, and the
+    stored rocprofv3 figures for its kernels."""
+    res = bench.run(steps, warmup)
+    wdt = "fp8" if quantised(cfg) else "bf16"
+    name = cfg["name"]
+    gb, gf = gateup_work(cfg, bench.active)
+    db, df = down_work(cfg, bench.active)
+    lb, lf = layer_work(cfg, bench.active)
+    step_s = res["ms_per_step"] / 1e3
+    rl = roofline(gb, gf, res["gateup_ms"] / 1e3, wdt, stored_figure(name))
+    drl = roofline(db, df, res["down_ms"] / 1e3, wdt)
+    return {
+        "workload": describe(cfg),
+        "value": round(cfg["T"] / step_s, 1), "unit": "tokens/s",
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "ms_per_step_mean": round(res["ms_per_step_mean"], 4),
+        "steps": steps, "warmup": warmup,
+        "dtype": "mxfp4 x e4m3" if cfg["w_dtype"] == "mxfp4" else wdt,
+        "active_experts": bench.active, "max_over_mean_load": round(bench.max_over_mean, 4),
+        "roofline": dict(rl, kernel=gateup_kernel(cfg), launch_ms=round(res["gateup_ms"], 4),
+                         algorithmic_bytes=gb, algorithmic_flops=gf,
+                         mfma_busy=stored_figure(name, "mfma", key="gateup_mfma_busy"),
+                         clock_ghz=stored_figure(name, "mfma", key="gateup_clock_ghz")),
+        "down_roofline": dict(drl, launch_ms=round(res["down_ms"], 4), algorithmic_bytes=db,
+                              algorithmic_flops=df,
+                              mfma_busy=stored_figure(name, "mfma", key="down_mfma_busy"),
+                              clock_ghz=stored_figure(name, "mfma", key="down_clock_ghz")),
+        "layer": {"pct_hbm": round(lb / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "pct_mfma": round(lf / step_s / 1e12 / MFMA_PEAK_TFLOPS[wdt], 4),
+                  "algorithmic_bytes": lb, "flops": lf,
+                  "design_overhead_bytes": design_overhead(cfg),
+                  "stages_ms": res["stages_ms"]},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -642,7 +748,10 @@ def main():
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "prefill", "skewed", "fp8", "mxfp4", "mxfp4_prefill"])
     ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill and skewed lines (decode runs)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the fp8 line (decode runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-residual", action="store_true",
                     help="skip timing the block with its fused residual step")
@@ -692,24 +801,20 @@ def main():
     progress(f"{args.workload}: inputs and weights")
     bench = Bench(cfg, dev)
     progress(f"{args.workload}: {args.warmup} warmup + {args.steps} timed steps")
-    res = bench.run(args.steps, args.warmup)
-    wdt = "fp8" if cfg["w_dtype"] in ("fp8", "mxfp4") else "bf16"
-    gb, gf = gateup_work(cfg, bench.active)
-    rl = roofline(gb, gf, res["gateup_ms"] / 1e3, wdt, stored_figure(cfg["name"]))
-    lb, lf = layer_work(cfg, bench.active)
-    step_s = res["ms_per_step"] / 1e3
+    main_line = workload_line(cfg, bench, args.steps, args.warmup)
     line = {
         "metric": METRIC,
-        "value": round(cfg["T"] / step_s, 1),
+        "value": main_line["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(res["ms_per_step"], 4),
+        "ms_per_step": main_line["ms_per_step"],
+        "ms_per_step_mean": main_line["ms_per_step_mean"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4 x e4m3" if cfg["w_dtype"] == "mxfp4" else wdt,
+        "dtype": main_line["dtype"],
         "data": "synthetic",
         "device": {"name": torch.cuda.get_device_name(0),
                    "arch": torch.cuda.get_device_properties(0).gcnArchName,
@@ -719,13 +824,9 @@ def main():
                    "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "top_k": cfg["top_k"],
                    "active_experts": bench.active, "max_over_mean_load": round(bench.max_over_mean, 4),
                    "parallelism": "single GPU"},
-        "roofline": dict(rl, kernel=gateup_kernel(cfg), launch_ms=round(res["gateup_ms"], 4),
-                         algorithmic_bytes=gb, algorithmic_flops=gf,
-                         mfma_busy=stored_figure(cfg["name"], "mfma", key="gateup_mfma_busy"),
-                         clock_ghz=stored_figure(cfg["name"], "mfma", key="gateup_clock_ghz")),
-        "layer": {"pct_hbm": round(lb / step_s / 1e9 / HBM_PEAK_GBS, 4),
-                  "pct_mfma": round(lf / step_s / 1e12 / MFMA_PEAK_TFLOPS[wdt], 4),
-                  "algorithmic_bytes": lb, "flops": lf, "stages_ms": res["stages_ms"]},
+        "roofline": main_line["roofline"],
+        "down_roofline": main_line["down_roofline"],
+        "layer": main_line["layer"],
     }
     if not args.no_residual:
         # the same block with the fused post-norm + depth-scaled residual step
@@ -738,29 +839,14 @@ def main():
             "step": 105, "ms_per_step": round(rres["ms_per_step"], 4),
             "value": round(cfg["T"] / (rres["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
             "combine_ms": rres["stages_ms"].get("combine"),
-            "plain_combine_ms": res["stages_ms"].get("combine")}
+            "plain_combine_ms": main_line["layer"]["stages_ms"].get("combine")}
     if args.workload == "decode" and not args.no_prefill:
-        pcfg = workloads.workload("prefill")
-        progress("prefill")
-        pb = Bench(pcfg, dev, weights=bench.w, packed=bench.pw)
-        pres = pb.run(args.prefill_steps, 3)
-        pgb, pgf = gateup_work(pcfg, pb.active)
-        plb, plf = layer_work(pcfg, pb.active)
-        ps = pres["ms_per_step"] / 1e3
-        line["prefill"] = {
-            "workload": describe(pcfg), "value": round(pcfg["T"] / ps, 1), "unit": "tokens/s",
-            "ms_per_step": round(pres["ms_per_step"], 4), "steps": args.prefill_steps,
-            "max_over_mean_load": round(pb.max_over_mean, 4),
-            "roofline": dict(roofline(pgb, pgf, pres["gateup_ms"] / 1e3, "bf16", stored_figure("prefill")),
-                             kernel=gateup_kernel(pcfg), launch_ms=round(pres["gateup_ms"], 4),
-                             algorithmic_bytes=pgb, algorithmic_flops=pgf,
-                             mfma_busy=stored_figure("prefill", "mfma", key="gateup_mfma_busy"),
-                             clock_ghz=stored_figure("prefill", "mfma", key="gateup_clock_ghz")),
-            "layer": {"pct_hbm": round(plb / ps / 1e9 / HBM_PEAK_GBS, 4),
-                      "pct_mfma": round(plf / ps / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-                      "stages_ms": pres["stages_ms"]},
-        }
-        del pb
+        for name, steps in (("prefill", args.prefill_steps), ("skewed", args.prefill_steps)):
+            progress(name)
+            wb = Bench(workloads.workload(name), dev, weights=bench.w, packed=bench.pw)
+            line[name] = workload_line(wb.cfg, wb, steps, 3)
+            del wb
+            torch.cuda.empty_cache()
     if args.workload == "decode" and not args.no_shard:
         progress("expert shard")
         line["ep_shard"] = ep_shard_line(dev, bench)
@@ -768,6 +854,14 @@ def main():
         progress("backward")
         line["backward"] = backward_line(workloads.workload("prefill"), dev, bench.w,
                                          args.backward_steps, bench.pw)
+        torch.cuda.empty_cache()
+    if args.workload == "decode" and not args.no_fp8:
+        progress("fp8: weights")
+        fcfg = workloads.workload("fp8")
+        fb = Bench(fcfg, dev)
+        progress("fp8")
+        line["fp8"] = workload_line(fcfg, fb, args.prefill_steps, 3)
+        del fb
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         n_cpu = args.cpu_tokens or (4 if cfg["w_dtype"] == "mxfp4" else 64)

@@ -8,6 +8,14 @@ raise instead of falling back to anything else.
 
 Names follow the Beam model doc's config fields: n_group, topk_group,
 routed_scaling_factor (transformers model doc "Beam", "Overview").
+
+Streams: every call takes ``stream`` (default: the current stream of the
+tensors' device) and enqueues its kernels there. Tensors a call allocates
+(outputs, and the workspace when none is passed) come from that stream's
+pool of torch's caching allocator, so a block freed on return is reused only
+by later work on the same stream, which runs after the kernels that used it.
+A caller that passes its own workspace or outputs owns their stream
+ordering, as for any torch tensor used on a side stream.
 """
 
 import ctypes
@@ -148,13 +156,15 @@ def pack_weights(w, out=None, stream=None):
     forward(..., packed=True)."""
     if w.dim() != 3 or not w.is_contiguous() or w.dtype not in _W_DTYPES:
         raise ValueError("pack_weights needs a contiguous [E, rows, cols] bf16/fp8/MXFP4 tensor")
+    s = _target(w.device, stream)
     if out is None:
-        out = torch.empty_like(w)
+        with torch.cuda.stream(s):
+            out = torch.empty_like(w)
     E, R, C = w.shape
     if w.dtype == torch.uint8:
         C *= 2  # weights per row
     st = lib().beam_moe_pack_weights(_ptr(w), _ptr(out), E, R, C, _W_DTYPES[w.dtype],
-                                     _stream(w.device, stream))
+                                     _handle(s))
     if st != BEAM_OK:
         raise BeamMoeError(st, "beam_moe_pack_weights")
     return out
@@ -164,11 +174,12 @@ def pack_mx_scales(s, out=None, stream=None):
     """Packed copy of row-major MXFP4 scale bytes s [E, R, C/32] (uint8, E8M0)."""
     if s.dim() != 3 or not s.is_contiguous() or s.dtype != torch.uint8:
         raise ValueError("pack_mx_scales needs a contiguous [E, rows, cols/32] uint8 tensor")
+    ts = _target(s.device, stream)
     if out is None:
-        out = torch.empty_like(s)
+        with torch.cuda.stream(ts):
+            out = torch.empty_like(s)
     E, R, B = s.shape
-    st = lib().beam_moe_pack_weights(_ptr(s), _ptr(out), E, R, 32 * B, BEAM_E8M0,
-                                     _stream(s.device, stream))
+    st = lib().beam_moe_pack_weights(_ptr(s), _ptr(out), E, R, 32 * B, BEAM_E8M0, _handle(ts))
     if st != BEAM_OK:
         raise BeamMoeError(st, "beam_moe_pack_weights")
     return out
@@ -194,14 +205,19 @@ def _check(t, name, shape, dtypes, device):
 
 
 def _workspace(cfg, T, device, workspace):
+    """The caller's workspace, or a new one (call it under the target stream)."""
     need = workspace_bytes(cfg, T)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     return workspace
 
 
-def _stream(device, stream):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
+def _target(device, stream):
+    """The torch stream a call runs on: ``stream``, else the device's current one."""
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _handle(s):
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -216,14 +232,16 @@ def route(x, router_w, expert_bias, *, n_group=8, topk_group=4, top_k=8,
     _check(router_w, "router_w", (E, H), (torch.float32,), dev)
     _check(expert_bias, "expert_bias", (E,), (torch.float32,), dev)
     cfg = make_config(H, 128, E, n_group, topk_group, top_k, 1.0, x.dtype, torch.bfloat16)
-    idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if return_logits else None
-    counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
-    ws = _workspace(cfg, T, dev, workspace)
+    s = _target(dev, stream)
+    with torch.cuda.stream(s):
+        idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev) if return_logits else None
+        counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
+        ws = _workspace(cfg, T, dev, workspace)
     st = lib().beam_moe_route(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
                               _ptr(idx), _ptr(w), _ptr(logits), _ptr(counts), _ptr(ws),
-                              ws.numel(), _stream(dev, stream))
+                              ws.numel(), _handle(s))
     if st != BEAM_OK:
         raise BeamMoeError(st, "beam_moe_route")
     return {"topk_idx": idx, "topk_w": w, "router_logits": logits, "expert_counts": counts}
@@ -305,31 +323,33 @@ def _forward(x, router_w, expert_bias, w_gate, w_up, w_down, res, scales, n_grou
             _check(sd, "w_down_scale", (n_w, H), (torch.float32,), dev)
     cfg = make_config(H, I, E, n_group, topk_group, top_k, routed_scaling_factor, x.dtype,
                       w_gate.dtype, packed)
-    if out is None:
-        out = torch.empty((T, H), dtype=x.dtype, device=dev)
-    else:
+    if out is not None:
         _check(out, "out", (T, H), (x.dtype,), dev)
+    s = _target(dev, stream)
     idx = w = counts = logits = None
-    if return_routing:
-        idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
-        w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
-        counts = torch.empty((E,), dtype=torch.int32, device=dev)
-    if return_logits:
-        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    ws = _workspace(cfg, T, dev, workspace)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty((T, H), dtype=x.dtype, device=dev)
+        if return_routing:
+            idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+            w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+            counts = torch.empty((E,), dtype=torch.int32, device=dev)
+        if return_logits:
+            logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        ws = _workspace(cfg, T, dev, workspace)
     if shard is not None:
         st = lib().beam_moe_forward_shard(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w),
                                           _ptr(expert_bias), shard[0], shard[1], _ptr(w_gate),
                                           _ptr(w_up), _ptr(w_down), _ptr(sg), _ptr(su), _ptr(sd),
                                           _ptr(out), _ptr(idx), _ptr(w), _ptr(counts), _ptr(ws),
-                                          ws.numel(), _stream(dev, stream))
+                                          ws.numel(), _handle(s))
         where = "beam_moe_forward_shard"
     elif res is None:
         st = lib().beam_moe_forward(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w),
                                     _ptr(expert_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                     _ptr(sg), _ptr(su), _ptr(sd), _ptr(out), _ptr(idx), _ptr(w),
                                     _ptr(counts), _ptr(logits), _ptr(ws), ws.numel(),
-                                    _stream(dev, stream))
+                                    _handle(s))
         where = "beam_moe_forward"
     else:
         st = lib().beam_moe_forward_residual(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w),
@@ -337,7 +357,7 @@ def _forward(x, router_w, expert_bias, w_gate, w_up, w_down, res, scales, n_grou
                                              _ptr(w_down), _ptr(sg), _ptr(su), _ptr(sd),
                                              ctypes.byref(res), _ptr(out), _ptr(idx), _ptr(w),
                                              _ptr(counts), _ptr(logits), _ptr(ws), ws.numel(),
-                                             _stream(dev, stream))
+                                             _handle(s))
         where = "beam_moe_forward_residual"
     if st != BEAM_OK:
         raise BeamMoeError(st, where)
@@ -353,10 +373,12 @@ def pack_weights_transposed(w, out=None, stream=None):
     if w.dtype != torch.bfloat16 or w.dim() != 3 or not w.is_contiguous():
         raise ValueError("expects a contiguous [E, rows, cols] bf16 tensor")
     E, R, C = w.shape
+    s = _target(w.device, stream)
     if out is None:
-        out = torch.empty((E, C, R), dtype=w.dtype, device=w.device)
+        with torch.cuda.stream(s):
+            out = torch.empty((E, C, R), dtype=w.dtype, device=w.device)
     st = lib().beam_moe_pack_weights_transposed(_ptr(w), _ptr(out), E, R, C, BEAM_BF16,
-                                                _stream(w.device, stream))
+                                                _handle(s))
     if st != BEAM_OK:
         raise BeamMoeError(st, "beam_moe_pack_weights_transposed")
     return out
@@ -388,26 +410,28 @@ def backward(x, router_w, expert_bias, w_gate, w_up, w_gate_t, w_up_t, w_down_t,
         _check(t, name, shape, (torch.bfloat16,), dev)
     cfg = make_config(H, I, E, n_group, topk_group, top_k, routed_scaling_factor, x.dtype,
                       torch.bfloat16, packed=True)
-    dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    drw = torch.empty((E, H), dtype=torch.float32, device=dev) if router_grad else None
+    need = backward_workspace_bytes(cfg, T, weight_grads)
+    if need == 0 and T > 0:
+        raise BeamMoeError(BEAM_ERR_CONFIG, "beam_moe_backward_workspace_bytes")
+    s = _target(dev, stream)
     dwg = dwu = dwd = None
-    if weight_grads:
-        dwg = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
-        dwu = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
-        dwd = torch.empty((E, H, I), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.stream(s):
+        dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        drw = torch.empty((E, H), dtype=torch.float32, device=dev) if router_grad else None
+        if weight_grads:
+            dwg = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
+            dwu = torch.empty((E, I, H), dtype=torch.bfloat16, device=dev)
+            dwd = torch.empty((E, H, I), dtype=torch.bfloat16, device=dev)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     grads = BeamMoeGrads(dx.data_ptr(), drw.data_ptr() if drw is not None else None,
                          dwg.data_ptr() if dwg is not None else None,
                          dwu.data_ptr() if dwu is not None else None,
                          dwd.data_ptr() if dwd is not None else None)
-    need = backward_workspace_bytes(cfg, T, weight_grads)
-    if need == 0 and T > 0:
-        raise BeamMoeError(BEAM_ERR_CONFIG, "beam_moe_backward_workspace_bytes")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     st = lib().beam_moe_backward(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w), _ptr(expert_bias),
                                  _ptr(w_gate), _ptr(w_up), _ptr(w_gate_t), _ptr(w_up_t),
                                  _ptr(w_down_t), _ptr(dout), ctypes.byref(grads), _ptr(workspace),
-                                 workspace.numel(), _stream(dev, stream))
+                                 workspace.numel(), _handle(s))
     if st != BEAM_OK:
         raise BeamMoeError(st, "beam_moe_backward")
     return {"dx": dx, "d_router_w": drw, "d_w_gate": dwg, "d_w_up": dwu, "d_w_down": dwd}
@@ -420,7 +444,7 @@ def update_bias(expert_bias, expert_counts, gamma, stream=None):
     _check(expert_bias, "expert_bias", (256,), (torch.float32,), dev)
     _check(expert_counts, "expert_counts", (256,), (torch.int32,), dev)
     st = lib().beam_moe_update_bias(_ptr(expert_bias), _ptr(expert_counts), 256, float(gamma),
-                                    _stream(dev, stream))
+                                    _handle(_target(dev, stream)))
     if st != BEAM_OK:
         raise BeamMoeError(st, "beam_moe_update_bias")
     return expert_bias

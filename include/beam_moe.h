@@ -149,7 +149,8 @@ size_t beam_moe_workspace_bytes(const beam_moe_config* cfg, int32_t T);
  *   expert_counts out [n_experts] int32 tokens per expert, or NULL.
  *   workspace     device scratch of at least beam_moe_workspace_bytes(cfg, T).
  * Errors: BEAM_ERR_NULL if cfg, x, router_w, expert_bias, topk_idx or topk_w
- * is NULL (or workspace when T > 0); see the conventions above.
+ * is NULL; BEAM_ERR_WORKSPACE if workspace is NULL or smaller than
+ * beam_moe_workspace_bytes() (T > 0); see the conventions above.
  */
 beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
                            const float* router_w, const float* expert_bias,
@@ -179,7 +180,8 @@ beam_status beam_moe_route(const beam_moe_config* cfg, int32_t T, const void* x,
  *   router_logits_out out [T, n_experts] fp32 or NULL.
  *   workspace     device scratch of at least beam_moe_workspace_bytes(cfg, T).
  * Errors: BEAM_ERR_NULL if cfg, x, router_w, expert_bias, w_gate, w_up, w_down
- * or out is NULL (or workspace when T > 0); BEAM_ERR_DTYPE if fp8 scales are
+ * or out is NULL; BEAM_ERR_WORKSPACE if workspace is NULL or smaller than
+ * beam_moe_workspace_bytes() (T > 0); BEAM_ERR_DTYPE if fp8 scales are
  * missing; see the conventions above.
  */
 beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* x,

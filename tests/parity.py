@@ -58,28 +58,123 @@ def run_forward(x, rw, b, w, cfg, **kw):
     return out, r
 
 
+# Decode tables: the oracle's own decoders applied once to every code, then
+# indexed with torch's multithreaded CPU gather (the same values as calling
+# the decoders on each weight, many times faster at 13M weights per matrix).
+_E4M3_TABLE = None
+_MX_TABLES = None
+
+
+def _e4m3_table():
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = oracle.e4m3.decode(np.arange(256, dtype=np.uint8))
+    return _E4M3_TABLE
+
+
+def _mx_tables():
+    """(byte -> (value of the low nibble, value of the high nibble), E8M0 byte -> scale)."""
+    global _MX_TABLES
+    if _MX_TABLES is None:
+        b = np.arange(256)
+        pair = np.stack([oracle.mxfp4.decode_e2m1(b & 0xF), oracle.mxfp4.decode_e2m1(b >> 4)], axis=1)
+        _MX_TABLES = (pair, oracle.mxfp4.decode_e8m0(b))
+    return _MX_TABLES
+
+
+def e4m3_dequantize(codes, scales):
+    """oracle.e4m3.decode(codes) * scales[:, None] through the decode table
+    (codes uint8 [R, C], per-row scales [R]; CPU tensors or arrays)."""
+    tab = torch.from_numpy(_e4m3_table())
+    c = torch.as_tensor(codes).to(torch.int64)
+    return (tab[c] * torch.as_tensor(scales).to(torch.float64)[:, None]).numpy()
+
+
+def mx_dequantize(packed, scales):
+    """oracle.mxfp4.dequantize through the decode tables."""
+    pair, e8 = (torch.from_numpy(t) for t in _mx_tables())
+    p = torch.as_tensor(packed).to(torch.int64)
+    v = pair[p].reshape(p.shape[0], -1)
+    R, K = v.shape
+    sc = e8[torch.as_tensor(scales).to(torch.int64)]
+    return (v.reshape(R, K // 32, 32) * sc[..., None]).reshape(R, K).numpy()
+
+
 def expert_getter(w):
     """get_expert(e) for the oracle: one expert copied to the host, float64
     (fp8 weights dequantised with their per-row scales, MXFP4 weights with
     their block scales; the row-major copies)."""
     fp8 = w["w_gate"].dtype == torch.float8_e4m3fn
     mx = is_mxfp4(w)
+    loaded = [0]
 
     def get(e):
+        loaded[0] += 1
+        if loaded[0] % 64 == 0:  # progress of a long full-shape reference
+            print(f"[oracle] {loaded[0]} experts loaded", flush=True)
         mats = []
         for k in ("w_gate", "w_up", "w_down"):
             m = w[k][e].to("cpu")
             if mx:
-                mats.append(oracle.mxfp4.dequantize(m.numpy(), w[k + "_scale"][e].to("cpu").numpy()))
+                mats.append(mx_dequantize(m, w[k + "_scale"][e].to("cpu")))
             elif fp8:
-                codes = m.view(torch.uint8).numpy()
-                sc = w[k + "_scale"][e].to("cpu").numpy().astype(np.float64)
-                mats.append(oracle.e4m3.decode(codes) * sc[:, None])
+                mats.append(e4m3_dequantize(m.view(torch.uint8), w[k + "_scale"][e].to("cpu")))
             else:
                 mats.append(m.to(torch.float64).numpy())
         return tuple(mats)
 
     return get
+
+
+def expert_rows(idx, E):
+    """The sorted order of the expert GEMMs, rebuilt from the routing: expert
+    e's rows are the tokens that chose it, in ascending token order (the
+    permutation is stable by token). Returns a list of E int arrays."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    tok = np.repeat(np.arange(T), k)
+    e = idx.reshape(-1)
+    order = np.lexsort((tok, e))
+    counts = np.bincount(e, minlength=E)
+    return np.split(tok[order], np.cumsum(counts)[:-1])
+
+
+def tile_cover(idx, E, bm=128, seed=0):
+    """Tokens whose outputs include, for every expert and every M-tile of
+    ``bm`` sorted rows, the tile's first row, its last row and one seeded
+    random row. With bm = 128 this also covers every 256-row tile (two
+    128-row blocks, one per half of the tile's waves)."""
+    rng = np.random.default_rng(seed)
+    pick = set()
+    for rows in expert_rows(idx, E):
+        n = len(rows)
+        for m0 in range(0, n, bm):
+            m1 = min(m0 + bm, n) - 1
+            for q in (m0, m1, int(rng.integers(m0, m1 + 1))):
+                pick.add(int(rows[q]))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def tiles_covered(tokens, idx, E, bm):
+    """(covered, total): M-tiles of ``bm`` sorted rows (expert by expert)
+    holding at least one row of ``tokens``, counted independently of how
+    the tokens were chosen."""
+    tokens = set(int(t) for t in tokens)
+    covered = total = 0
+    for rows in expert_rows(idx, E):
+        for m0 in range(0, len(rows), bm):
+            total += 1
+            covered += any(int(t) in tokens for t in rows[m0:m0 + bm])
+    return covered, total
+
+
+def coverage_report(tokens, idx, E, bms=(128, 256)):
+    rep = {}
+    for bm in bms:
+        c, t = tiles_covered(tokens, idx, E, bm)
+        rep[f"tiles_covered_{bm}"] = c
+        rep[f"tiles_total_{bm}"] = t
+    return rep
 
 
 def check_routing(gpu_r, ora, cfg, report):

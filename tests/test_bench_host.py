@@ -38,15 +38,35 @@ def test_work_counts_match_the_block_sizes():
     assert weights == 20_132_659_200
     assert lb == weights + 2 * cfg["T"] * H * 2 + 256 * H * 4
     # the gate/up launch reads two of the three matrices of each active expert
+    # and the x rows; the h rows it writes are design overhead, not counted
     gb, gf = bench.gateup_work(cfg, 222)
-    assert gb - 222 * 2 * H * I * 2 == cfg["T"] * H * 2 + cfg["T"] * 8 * I * 2
+    assert gb - 222 * 2 * H * I * 2 == cfg["T"] * H * 2
     # flops: 2 per multiply-add, 8 experts per token, gate and up of I x H each
     assert gf == 2 * cfg["T"] * 8 * 2 * I * H
     assert lf == 1.5 * gf  # the down projection adds half again
-    # fp8: one byte per weight, e4m3 x in, fp32 h out
+    db, df = bench.down_work(cfg, 222)
+    assert db == 222 * H * I * 2 and df == gf / 2
+    # gate/up + down weights are the layer's weights
+    assert gb + db - cfg["T"] * H * 2 == 222 * 3 * H * I * 2
+    # fp8: one byte per weight, e4m3 x codes in
     f8 = workloads.workload("fp8")
     b8, _ = bench.gateup_work(f8, 256)
-    assert b8 == 256 * 2 * H * I + f8["T"] * H + f8["T"] * 8 * I * 4
+    assert b8 == 256 * 2 * H * I + f8["T"] * H
+
+
+def test_design_overhead_counts_the_round_trips():
+    # prefill: h (bf16) and y (bf16) each written once and read once
+    p = workloads.workload("prefill")
+    P, H, I = p["T"] * 8, p["hidden"], p["intermediate"]
+    o = bench.design_overhead(p)
+    assert o["h_round_trip"] == 2 * P * I * 2 and o["y_round_trip"] == 2 * P * H * 2
+    assert o["total"] == o["h_round_trip"] + o["y_round_trip"]
+    # the skewed workload's overhead is about 4 GB, the prefill one's about 1 GB
+    assert 0.9e9 < o["total"] < 1.1e9
+    assert 3.9e9 < bench.design_overhead(workloads.workload("skewed"))["total"] < 4.3e9
+    # quantised weights add the E4M3 codes of x and h
+    f = bench.design_overhead(workloads.workload("fp8"))
+    assert f["x_codes"] == 2 * 8192 * H and f["h_codes"] == 2 * 8192 * 8 * I
 
 
 def _write_counters(path, rows):

@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads
 import group_limited_routing_amd as gl
-from parity import check_routing, expert_getter, output_errors
+from parity import check_routing, coverage_report, expert_getter, output_errors, tile_cover
 
 pytestmark = pytest.mark.gpu
 
@@ -180,9 +180,11 @@ def test_update_bias_matches_oracle():
 
 def test_backward_prefill_full_shape():
     """Beam's prefill shape (T=4096, H=5120, I=2560, balanced bias): dx on
-    sampled tokens (the oracle with all their experts) and the weight
-    gradients of two experts (the oracle running only those experts, whose
-    weight gradients need no other expert)."""
+    a token set that holds the first, the last and a random row of every
+    M-tile of every expert (the oracle with all their experts), and the
+    complete weight gradients of eight experts (the busiest, the least busy
+    and six spread over the groups; the oracle runs only those experts,
+    whose weight gradients need no other expert)."""
     dev = _dev()
     cfg = workloads.workload("prefill")
     x, rw, b = workloads.make_small_inputs(cfg, 0)
@@ -196,22 +198,31 @@ def test_backward_prefill_full_shape():
     torch.cuda.empty_cache()
     rep = {"T": cfg["T"]}
     idx, r = _routing(cfg, x, rw, b, rep)
+    E = cfg["n_experts"]
     x64 = x.cpu().double().numpy()
     rw64 = rw.cpu().double().numpy()
     b64 = b.cpu().double().numpy()
     d64 = dout.cpu().double().numpy()
-    toks = np.array([0, 1, 2047, 4095])
+    gidx = r["topk_idx"].cpu().numpy()
+    toks = tile_cover(gidx, E, 128, seed=7)
+    cov = coverage_report(toks, gidx, E)
+    rep.update(cov)
+    for bm in (128, 256):
+        assert cov[f"tiles_covered_{bm}"] == cov[f"tiles_total_{bm}"], cov
+    rep["dx_tokens"] = int(len(toks))
     ref = oracle.backward.backward(x64[toks], rw64, b64, expert_getter(w), d64[toks], 8, 4, 8, 2.5,
                                    routing=idx[toks], weight_grads=False)
     check_grad("dx", g["dx"][torch.as_tensor(toks, device=dev)].cpu().double().numpy(), ref["dx"], rep)
     cnt = r["expert_counts"].cpu().numpy()
-    for e in (int(cnt.argmax()), 77):
-        tk = np.nonzero(np.any(idx == e, axis=1))[0]
-        refe = oracle.backward.backward(x64[tk], rw64, b64, expert_getter(w), d64[tk], 8, 4, 8,
-                                        2.5, routing=idx[tk], only_experts={e})
-        for name_ in ("d_w_gate", "d_w_up", "d_w_down"):
-            check_grad(name_, g[name_][e].cpu().double().numpy(), refe[name_][e], rep)
-        rep[f"expert_{e}_rows"] = int(len(tk))
+    live = np.nonzero(cnt)[0]
+    experts = sorted({int(cnt.argmax()), int(live[np.argmin(cnt[live])]), 0, 37, 77, 130, 201, 255})
+    tk = np.nonzero(np.any(np.isin(idx, experts), axis=1))[0]
+    refe = oracle.backward.backward(x64[tk], rw64, b64, expert_getter(w), d64[tk], 8, 4, 8, 2.5,
+                                    routing=idx[tk], only_experts=set(experts))
+    for name_ in ("d_w_gate", "d_w_up", "d_w_down"):
+        got = np.concatenate([g[name_][e].cpu().double().numpy() for e in experts])
+        check_grad(name_, got, np.concatenate([refe[name_][e] for e in experts]), rep)
+    rep["weight_grad_experts"] = {int(e): int(cnt[e]) for e in experts}
     print("[backward] prefill full shape: " + json.dumps(rep), flush=True)
     del w, g
     torch.cuda.empty_cache()

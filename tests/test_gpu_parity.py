@@ -5,10 +5,13 @@ column tiles and have ragged tails (T, rows per expert and tiles not
 multiples of the tile sizes), and they exercise both expert-GEMM variants
 (weight streaming for few rows per expert, LDS tiles for many) and both
 weight formats. The named Beam workloads (decode T=64, prefill T=4096,
-skewed T=16384, fp8 T=8192) run at full size in the same launch
-configuration the benchmark times: routing is compared on every token and
-the outputs on sampled tokens, which the oracle computes one expert at a
-time.
+skewed T=16384, fp8 T=8192, MXFP4 T=64 and T=4096) run at full size in the
+same launch configuration the benchmark times: routing is compared on every
+token, and the outputs on every token at decode and, above that, on a set of
+tokens that holds the first, the last and a random row of every M-tile of
+every expert (tiles of 128 sorted rows, which also covers every 256-row
+tile), which the oracle computes one expert at a time. Each report prints
+the covered and total tile counts, and the test asserts they are equal.
 """
 
 import json
@@ -20,8 +23,8 @@ import torch
 import oracle
 import workloads
 import group_limited_routing_amd as gl
-from parity import (check_logits, check_outputs, check_routing, oracle_reference, run_forward,
-                    output_errors, packed_copy)
+from parity import (check_logits, check_outputs, check_routing, coverage_report, oracle_reference,
+                    run_forward, output_errors, packed_copy, tile_cover)
 
 pytestmark = pytest.mark.gpu
 
@@ -285,6 +288,23 @@ def test_single_token_and_empty():
     assert out.shape == (0, 256)
 
 
+# ------------------------------------------------- many M-tiles per expert, every token
+@pytest.mark.parametrize("w_dtype,I,packed", [("bf16", 256, False), ("bf16", 256, True),
+                                              ("fp8", 256, False), ("fp8", 256, True),
+                                              ("mxfp4", 512, True)])
+def test_hot_experts_span_many_mtiles(w_dtype, I, packed):
+    """The skewed routing (+0.5 bias on experts 0..7, all in group 0) at a
+    small width: each hot expert gets about two thirds of the 4000 tokens,
+    so its rows span 11 M-tiles of 256 (22 of 128). The tile order then runs
+    several full blocks of M-tiles and a partial last block per expert, and
+    every token's output is compared with the oracle."""
+    cfg = _case(4000, 512, I, w_dtype=w_dtype, bias="hot")
+    out, r = _full_compare(f"hot experts {w_dtype} I={I}" + (" packed" if packed else ""), cfg,
+                           25, packed)
+    cnt = r["expert_counts"].cpu().numpy()
+    assert cnt[:8].min() >= 9 * 256, cnt[:8]
+
+
 # ---------------------------------------------------------------- full Beam shape
 @pytest.fixture(scope="module")
 def beam_bf16_weights():
@@ -297,47 +317,6 @@ def beam_bf16_weights():
     torch.cuda.empty_cache()
 
 
-def _sample_tokens(r, near, T, hot=None, n=4):
-    idx = r["topk_idx"].cpu().numpy()
-    toks = list(range(min(n, T))) + [T - 1]
-    if hot is not None:
-        toks += list(np.nonzero(np.any(idx == hot, axis=1))[0][:2])
-    toks += list(np.nonzero(near)[0][:3])
-    return np.array(sorted(set(int(t) for t in toks)))
-
-
-def _full_shape(name, wl, w, extra=None, oracle_weights=None):
-    dev = _dev()
-    cfg = workloads.workload(wl)
-    x, rw, b = workloads.make_small_inputs(cfg, 0)
-    x, rw, b = x.to(dev), rw.to(dev), b.to(dev)
-    out, r = run_forward(x, rw, b, w, cfg)
-    w = oracle_weights if oracle_weights is not None else w
-    x64 = x.cpu().double().numpy()
-    rw64 = rw.cpu().double().numpy()
-    ora = oracle.route(x64, rw64, b.cpu().double().numpy(), 8, 4, 8)
-    rep = {"T": cfg["T"]}
-    near = check_routing(r, ora, cfg, rep)
-    cnt = r["expert_counts"].cpu().numpy()
-    rep["active_experts"] = int((cnt > 0).sum())
-    rep["max_over_mean"] = float(cnt.max() / cnt.mean())
-    tokens = _sample_tokens(r, near, cfg["T"], hot=int(cnt.argmax()))
-    ref = oracle_reference(tokens, x, rw, b, w, cfg, r["topk_idx"].cpu().numpy(), near)
-    check_outputs(out[torch.as_tensor(tokens, device=dev)].cpu().double().numpy(), ref, rep)
-    rep["sampled_tokens"] = len(tokens)
-    if extra:
-        extra(rep, cnt, out)
-    _report(name, rep)
-
-
-def test_beam_decode_full_shape(beam_bf16_weights):
-    _full_shape("decode T=64", "decode", beam_bf16_weights)
-
-
-def test_beam_decode_full_shape_packed(beam_bf16_weights, beam_bf16_packed):
-    _full_shape("decode T=64 packed", "decode", beam_bf16_packed, oracle_weights=beam_bf16_weights)
-
-
 @pytest.fixture(scope="module")
 def beam_bf16_packed(beam_bf16_weights):
     pw = packed_copy(beam_bf16_weights)
@@ -347,25 +326,75 @@ def beam_bf16_packed(beam_bf16_weights):
     torch.cuda.empty_cache()
 
 
-def _pick(packed, w, pw):
-    return (pw, w) if packed else (w, None)
+def _full_shape(name, wl, variants, oracle_weights, extra=None, all_tokens=False):
+    """Run the workload's forward once per weight variant (label, weights):
+    routing compared on every token (and equal across the variants); the
+    outputs of every variant on the compared tokens against one oracle pass
+    (all tokens, or a set covering every M-tile of every expert)."""
+    dev = _dev()
+    cfg = workloads.workload(wl)
+    T, E = cfg["T"], cfg["n_experts"]
+    print(f"\n[parity] {name}: T={T} variants {[v[0] for v in variants]}", flush=True)
+    x, rw, b = workloads.make_small_inputs(cfg, 0)
+    x, rw, b = x.to(dev), rw.to(dev), b.to(dev)
+    runs = []
+    for label, w in variants:
+        out, r = run_forward(x, rw, b, w, cfg)
+        runs.append((label, out, r))
+    r0 = runs[0][2]
+    for label, _, r in runs[1:]:
+        for k in ("topk_idx", "topk_w", "expert_counts", "router_logits"):
+            assert torch.equal(r[k], r0[k]), (label, k)
+    x64 = x.cpu().double().numpy()
+    rw64 = rw.cpu().double().numpy()
+    ora = oracle.route(x64, rw64, b.cpu().double().numpy(), cfg["n_group"], cfg["topk_group"],
+                       cfg["top_k"])
+    rep = {"T": T}
+    near = check_routing(r0, ora, cfg, rep)
+    gidx = r0["topk_idx"].cpu().numpy()
+    cnt = r0["expert_counts"].cpu().numpy()
+    rep["active_experts"] = int((cnt > 0).sum())
+    rep["max_over_mean"] = float(cnt.max() / cnt.mean())
+    if all_tokens:
+        tokens = np.arange(T)
+    else:
+        tokens = np.union1d(tile_cover(gidx, E, 128, seed=T), np.nonzero(near)[0])
+    cov = coverage_report(tokens, gidx, E)
+    rep.update(cov)
+    for bm in (128, 256):
+        assert cov[f"tiles_covered_{bm}"] == cov[f"tiles_total_{bm}"], cov
+    rep["compared_tokens"] = int(len(tokens))
+    ref = oracle_reference(tokens, x, rw, b, oracle_weights, cfg, gidx, near)
+    sel = torch.as_tensor(tokens, device=dev)
+    for label, out, _ in runs:
+        check_outputs(out[sel].cpu().double().numpy(), ref, rep, label + "_")
+    if extra:
+        extra(rep, cnt)
+    _report(name, rep)
 
 
-@pytest.mark.parametrize("packed", LAYOUTS)
-def test_beam_prefill_full_shape(beam_bf16_weights, beam_bf16_packed, packed):
-    def balanced(rep, cnt, out):
+def test_beam_decode_full_shape(beam_bf16_weights, beam_bf16_packed):
+    """T=64: every token, row-major and packed weights."""
+    _full_shape("decode T=64", "decode",
+                [("rowmajor", beam_bf16_weights), ("packed", beam_bf16_packed)],
+                beam_bf16_weights, all_tokens=True)
+
+
+def test_beam_prefill_full_shape(beam_bf16_weights, beam_bf16_packed):
+    def balanced(rep, cnt):
         assert rep["max_over_mean"] <= 1.05
-    w, ow = _pick(packed, beam_bf16_weights, beam_bf16_packed)
-    _full_shape("prefill T=4096" + (" packed" if packed else ""), "prefill", w, balanced, ow)
+    _full_shape("prefill T=4096", "prefill",
+                [("rowmajor", beam_bf16_weights), ("packed", beam_bf16_packed)],
+                beam_bf16_weights, balanced)
 
 
-@pytest.mark.parametrize("packed", LAYOUTS)
-def test_beam_skewed_full_shape(beam_bf16_weights, beam_bf16_packed, packed):
-    def skewed(rep, cnt, out):
+def test_beam_skewed_full_shape(beam_bf16_weights, beam_bf16_packed):
+    def skewed(rep, cnt):
         assert cnt[:8].min() >= 4 * cnt.mean()   # the +0.5 bias makes experts 0-7 hot
         assert int(cnt.sum()) == 8 * 16384
-    w, ow = _pick(packed, beam_bf16_weights, beam_bf16_packed)
-    _full_shape("skewed T=16384" + (" packed" if packed else ""), "skewed", w, skewed, ow)
+    _full_shape("skewed T=16384", "skewed",
+                [("rowmajor", beam_bf16_weights), ("packed", beam_bf16_packed)],
+                beam_bf16_weights, skewed)
 
 
 def test_beam_mxfp4_decode_full_shape():
@@ -375,7 +404,7 @@ def test_beam_mxfp4_decode_full_shape():
     pw = packed_copy(w)
     torch.cuda.synchronize()
     try:
-        _full_shape("mxfp4 decode T=64 packed", "mxfp4", pw, oracle_weights=w)
+        _full_shape("mxfp4 decode T=64", "mxfp4", [("packed", pw)], w, all_tokens=True)
     finally:
         del w, pw
         torch.cuda.empty_cache()
@@ -388,7 +417,7 @@ def test_beam_mxfp4_prefill_full_shape():
     pw = packed_copy(w)
     torch.cuda.synchronize()
     try:
-        _full_shape("mxfp4 prefill T=4096 packed", "mxfp4_prefill", pw, oracle_weights=w)
+        _full_shape("mxfp4 prefill T=4096", "mxfp4_prefill", [("packed", pw)], w)
     finally:
         del w, pw
         torch.cuda.empty_cache()
@@ -401,8 +430,7 @@ def test_beam_fp8_full_shape():
     pw8 = packed_copy(w8)
     torch.cuda.synchronize()
     try:
-        _full_shape("fp8 T=8192", "fp8", w8)
-        _full_shape("fp8 T=8192 packed", "fp8", pw8, oracle_weights=w8)
+        _full_shape("fp8 T=8192", "fp8", [("rowmajor", w8), ("packed", pw8)], w8)
     finally:
         del w8, pw8
         torch.cuda.empty_cache()

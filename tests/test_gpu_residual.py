@@ -135,6 +135,6 @@ def test_residual_matches_unfused_routing():
 @pytest.mark.parametrize("wl", ["decode", "mxfp4"])
 def test_residual_full_decode_shape(wl):
     """Beam's decode shape (T=64, H=5120, I=2560) with packed weights, step
-    105; outputs of sampled tokens against the oracle."""
+    105; the outputs of every token against the oracle."""
     cfg = workloads.workload(wl)
-    _run(f"{wl} full shape", cfg, 0, 105, packed=True, tokens=np.array([0, 1, 31, 63]))
+    _run(f"{wl} full shape", cfg, 0, 105, packed=True)

@@ -35,7 +35,10 @@ EXPORTED = ("beam_moe_workspace_bytes", "beam_moe_route", "beam_moe_forward",
             "beam_moe_forward_residual", "beam_moe_status_string", "beam_moe_profile_begin",
             "beam_moe_profile_end", "beam_moe_pack_weights", "beam_moe_backward_workspace_bytes",
             "beam_moe_backward", "beam_moe_pack_weights_transposed", "beam_moe_update_bias",
-            "beam_moe_forward_shard")
+            "beam_moe_forward_shard", "beam_moe_forward_noalloc")
+
+# Scratch size of beam_moe_forward_noalloc (BEAM_MOE_NOALLOC_MAX_BYTES in the header)
+NOALLOC_MAX_BYTES = 64 << 20
 
 STAGES = ("router_logits", "select", "perm_hist", "perm_scan", "perm_scatter", "quant_x",
           "gateup", "quant_h", "down", "combine", "bwd_gateup", "bwd_down", "bwd_dx",
@@ -117,6 +120,9 @@ def lib():
         L.beam_moe_forward_shard.argtypes = [cfgp, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, vp, sz, vp]
         L.beam_moe_forward_shard.restype = ctypes.c_int
+        L.beam_moe_forward_noalloc.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, vp, vp, vp, vp]
+        L.beam_moe_forward_noalloc.restype = ctypes.c_int
         L.beam_moe_backward_workspace_bytes.argtypes = [cfgp, i32, i32]
         L.beam_moe_backward_workspace_bytes.restype = sz
         L.beam_moe_backward.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -277,6 +283,53 @@ def forward_residual(x, router_w, expert_bias, w_gate, w_up, w_down, stream_in, 
     return _forward(x, router_w, expert_bias, w_gate, w_up, w_down, res, scales, n_group,
                     topk_group, top_k, routed_scaling_factor, out, return_routing,
                     return_logits, workspace, stream, packed)
+
+
+def forward_noalloc(x, router_w, expert_bias, w_gate, w_up, w_down, *, out, scales=None,
+                    n_group=8, topk_group=4, top_k=8, routed_scaling_factor=2.5, topk_idx=None,
+                    topk_w=None, expert_counts=None, router_logits=None, stream=None,
+                    packed=False):
+    """The whole MoE block through beam_moe_forward_noalloc: the library's
+    static per-GPU scratch instead of a workspace. Every output is the
+    caller's (``out`` [T, H] in x's dtype, and optionally topk_idx [T, k]
+    int32, topk_w [T, k] fp32, expert_counts [E] int32, router_logits [T, E]
+    fp32), so the call allocates nothing. Calls that overlap on one GPU
+    race on the shared scratch. Other arguments as for forward()."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    I = w_gate.shape[1]
+    dev = x.device
+    mx = w_gate.dtype == torch.uint8
+    d = 2 if mx else 1
+    wdt = (torch.bfloat16, torch.float8_e4m3fn, torch.uint8)
+    _check(x, "x", (T, H), (torch.float32, torch.bfloat16), dev)
+    _check(router_w, "router_w", (E, H), (torch.float32,), dev)
+    _check(expert_bias, "expert_bias", (E,), (torch.float32,), dev)
+    _check(w_gate, "w_gate", (E, I, H // d), wdt, dev)
+    _check(w_up, "w_up", (E, I, H // d), (w_gate.dtype,), dev)
+    _check(w_down, "w_down", (E, H, I // d), (w_gate.dtype,), dev)
+    _check(out, "out", (T, H), (x.dtype,), dev)
+    for t, name, shape, dt in ((topk_idx, "topk_idx", (T, top_k), torch.int32),
+                               (topk_w, "topk_w", (T, top_k), torch.float32),
+                               (expert_counts, "expert_counts", (E,), torch.int32),
+                               (router_logits, "router_logits", (T, E), torch.float32)):
+        if t is not None:
+            _check(t, name, shape, (dt,), dev)
+    sg = su = sd = None
+    if w_gate.dtype in (torch.float8_e4m3fn, torch.uint8):
+        if scales is None:
+            raise ValueError("quantised weights need (w_gate_scale, w_up_scale, w_down_scale)")
+        sg, su, sd = scales
+    cfg = make_config(H, I, E, n_group, topk_group, top_k, routed_scaling_factor, x.dtype,
+                      w_gate.dtype, packed)
+    st = lib().beam_moe_forward_noalloc(ctypes.byref(cfg), T, _ptr(x), _ptr(router_w),
+                                        _ptr(expert_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                        _ptr(sg), _ptr(su), _ptr(sd), _ptr(out), _ptr(topk_idx),
+                                        _ptr(topk_w), _ptr(expert_counts), _ptr(router_logits),
+                                        _handle(_target(dev, stream)))
+    if st != BEAM_OK:
+        raise BeamMoeError(st, "beam_moe_forward_noalloc")
+    return out
 
 
 def forward_shard(x, router_w, expert_bias, expert_begin, expert_end, w_gate, w_up, w_down, *,

@@ -11,6 +11,12 @@
 #include "common.h"
 #include "internal.h"
 
+// Scratch of beam_moe_forward_noalloc: one array per GPU (each device holds
+// its own copy at its own address), from the library's load until the
+// process ends. Host code never passes this name to a kernel: there it is a
+// host-side stand-in; the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[BEAM_MOE_NOALLOC_MAX_BYTES];
+
 namespace beam {
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -346,6 +352,40 @@ const void* shard_base(const void* p, int e0, size_t stride_bytes) {
   return p ? (const void*)((uintptr_t)p - (uintptr_t)e0 * stride_bytes) : nullptr;
 }
 
+constexpr size_t kNoAllocScratchBytes = BEAM_MOE_NOALLOC_MAX_BYTES;
+
+// Device address of `scratch` on the device that runs `st`, looked up once
+// per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+beam_status scratch_address(hipStream_t st, void** out) {
+  int dev = -1, cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return BEAM_ERR_HIP;
+  if (st) {
+    if (hipStreamGetDevice(st, &dev) != hipSuccess) return BEAM_ERR_HIP;
+  } else {
+    dev = cur;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return BEAM_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return BEAM_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return BEAM_ERR_HIP;
+    if (e != hipSuccess || !p) return BEAM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BEAM_OK;
+}
+
+// Where the forward's workspace comes from: the caller's argument, or the
+// library's static per-device scratch (beam_moe_forward_noalloc).
+enum class WsSource { kCaller, kStatic };
+
 // The forward pass; with `res` set the final combine is the fused residual
 // step; with an expert range [e0, e1) other than all experts it is one
 // expert shard's share (its weights hold experts e0 .. e1 - 1 only).
@@ -356,7 +396,7 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
                          const beam_moe_residual* res, void* out, int32_t* topk_idx_out,
                          float* topk_w_out, int32_t* expert_counts_out, float* router_logits_out,
                          void* workspace, size_t workspace_bytes, void* stream, int e0 = 0,
-                         int e1 = kExperts) {
+                         int e1 = kExperts, WsSource wsrc = WsSource::kCaller) {
   const beam_status cs = check_config(cfg);
   if (cs != BEAM_OK) return cs;
   if (e0 < 0 || e1 > kExperts || e0 >= e1) return BEAM_ERR_CONFIG;
@@ -373,7 +413,7 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
   if (res && (misaligned(res->stream_in) || misaligned(res->norm_weight))) return BEAM_ERR_ALIGN;
   const bool fp8 = cfg->w_dtype == BEAM_FP8_E4M3 || cfg->w_dtype == BEAM_MXFP4;
   if (fp8 && (!w_gate_scale || !w_up_scale || !w_down_scale)) return BEAM_ERR_DTYPE;
-  if (!workspace) return BEAM_ERR_WORKSPACE;
+  if (wsrc == WsSource::kCaller && !workspace) return BEAM_ERR_WORKSPACE;
   if (misaligned(x) || misaligned(router_w) || misaligned(expert_bias) || misaligned(w_gate) ||
       misaligned(w_up) || misaligned(w_down) || misaligned(out) || misaligned(topk_idx_out) ||
       misaligned(topk_w_out) || misaligned(expert_counts_out) || misaligned(router_logits_out) ||
@@ -383,9 +423,16 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
   Shape s = shape_of(cfg, T);
   s.n_run = e1 - e0;
   const Layout L = make_layout(s);
+  hipStream_t st = (hipStream_t)stream;
+  if (wsrc == WsSource::kStatic) {
+    // every argument check is done; the size check is host arithmetic too
+    if (L.total > kNoAllocScratchBytes) return BEAM_ERR_WORKSPACE;
+    const beam_status ss = scratch_address(st, &workspace);
+    if (ss != BEAM_OK) return ss;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (workspace_bytes < L.total) return BEAM_ERR_WORKSPACE;
 
-  hipStream_t st = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   Buffers B = carve(L, workspace);
   int32_t* idx = topk_idx_out ? topk_idx_out : B.idx;
@@ -690,6 +737,19 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
   return forward_impl(cfg, T, x, router_w, expert_bias, w_gate, w_up, w_down, w_gate_scale,
                       w_up_scale, w_down_scale, nullptr, out, topk_idx_out, topk_w_out,
                       expert_counts_out, router_logits_out, workspace, workspace_bytes, stream);
+}
+
+beam_status beam_moe_forward_noalloc(const beam_moe_config* cfg, int32_t T, const void* x,
+                                     const float* router_w, const float* expert_bias,
+                                     const void* w_gate, const void* w_up, const void* w_down,
+                                     const void* w_gate_scale, const void* w_up_scale,
+                                     const void* w_down_scale, void* out, int32_t* topk_idx_out,
+                                     float* topk_w_out, int32_t* expert_counts_out,
+                                     float* router_logits_out, void* stream) {
+  return forward_impl(cfg, T, x, router_w, expert_bias, w_gate, w_up, w_down, w_gate_scale,
+                      w_up_scale, w_down_scale, nullptr, out, topk_idx_out, topk_w_out,
+                      expert_counts_out, router_logits_out, nullptr, 0, stream, 0, kExperts,
+                      WsSource::kStatic);
 }
 
 beam_status beam_moe_forward_shard(const beam_moe_config* cfg, int32_t T, const void* x,

@@ -194,6 +194,33 @@ beam_status beam_moe_forward(const beam_moe_config* cfg, int32_t T, const void* 
                              void* stream);
 
 /*
+ * beam_moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments, results and kernels as
+ * beam_moe_forward (minus workspace and workspace_bytes). Its scratch is a
+ * static array of BEAM_MOE_NOALLOC_MAX_BYTES in device memory, one per GPU
+ * the library runs on, held until the process ends; the call allocates and
+ * frees nothing. 64 MiB holds the forward's workspace for up to 256 tokens at
+ * Beam's shape (hidden 5120, intermediate 2560) with bf16, fp8 or MXFP4
+ * experts; larger problems return BEAM_ERR_WORKSPACE before any HIP call
+ * (beam_moe_workspace_bytes(cfg, T) tells the need). Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and give wrong results.
+ * No part of the scratch needs to start at zero. The first call on a device
+ * looks up the array's device address (hipGetSymbolAddress, the stream's
+ * device current) and keeps it; a failure there returns BEAM_ERR_HIP.
+ */
+#define BEAM_MOE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
+beam_status beam_moe_forward_noalloc(const beam_moe_config* cfg, int32_t T, const void* x,
+                                     const float* router_w, const float* expert_bias,
+                                     const void* w_gate, const void* w_up, const void* w_down,
+                                     const void* w_gate_scale, const void* w_up_scale,
+                                     const void* w_down_scale, void* out, int32_t* topk_idx_out,
+                                     float* topk_w_out, int32_t* expert_counts_out,
+                                     float* router_logits_out, void* stream);
+
+/*
  * One expert shard's share of the block, for expert parallelism (launch post
  * "Introducing Beam", section "Multi-GPU and multi-node": each expert lives
  * on one device; transformers model doc "Beam": ep_size). The routing is

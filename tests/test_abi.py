@@ -285,3 +285,39 @@ def test_library_links_every_kernel(L):
                    "pack_t_kernel", "bias_step_kernel", "quant_x_kernel",
                    "quant_h_kernel", "pack_kernel"]:
         assert f"__device_stub__{kernel}" in syms, kernel
+
+
+def _noalloc(L, cfg, T, **over):
+    p = dict(x=FAKE, rw=FAKE, b=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, sg=None, su=None, sd=None,
+             out=FAKE, idx=None, w=None, cnt=None, logits=None)
+    p.update(over)
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.beam_moe_forward_noalloc(ctypes.byref(cfg) if cfg is not None else None, T,
+                                      v(p["x"]), v(p["rw"]), v(p["b"]), v(p["wg"]), v(p["wu"]),
+                                      v(p["wd"]), v(p["sg"]), v(p["su"]), v(p["sd"]),
+                                      v(p["out"]), v(p["idx"]), v(p["w"]), v(p["cnt"]),
+                                      v(p["logits"]), None)
+
+
+def test_noalloc_checks_run_before_any_hip_call(L):
+    """beam_moe_forward_noalloc: the forward's checks, then the scratch limit,
+    all before its first HIP call. This machine has no GPU, so a HIP call
+    would return BEAM_ERR_HIP: the statuses below show the checks came
+    first."""
+    c = beam_cfg()
+    assert gl.NOALLOC_MAX_BYTES == 64 << 20
+    assert _noalloc(L, c, 0, x=None, out=None) == gl.BEAM_OK
+    assert _noalloc(L, None, 8) == gl.BEAM_ERR_NULL
+    assert _noalloc(L, beam_cfg(n_group=3), 8) == gl.BEAM_ERR_CONFIG
+    assert _noalloc(L, c, -1) == gl.BEAM_ERR_SHAPE
+    for name in ["x", "rw", "b", "wg", "wu", "wd", "out"]:
+        assert _noalloc(L, c, 8, **{name: None}) == gl.BEAM_ERR_NULL, name
+    assert _noalloc(L, c, 8, out=FAKE + 4) == gl.BEAM_ERR_ALIGN
+    assert _noalloc(L, beam_cfg(w_dtype=gl.BEAM_FP8_E4M3), 8) == gl.BEAM_ERR_DTYPE
+    # the scratch holds the workspace of every batch up to 256 tokens at
+    # Beam's shape, bf16 / fp8 / MXFP4 experts; beyond it the call refuses
+    for wdt in (gl.BEAM_BF16, gl.BEAM_FP8_E4M3):
+        assert gl.workspace_bytes(beam_cfg(w_dtype=wdt), 256) <= gl.NOALLOC_MAX_BYTES
+    big = next(T for T in range(256, 4096) if gl.workspace_bytes(c, T) > gl.NOALLOC_MAX_BYTES)
+    assert _noalloc(L, c, big) == gl.BEAM_ERR_WORKSPACE
+    assert _noalloc(L, c, 1 << 20) == gl.BEAM_ERR_WORKSPACE

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -32,7 +33,8 @@ Layout make_layout(const Shape& s) {
   const size_t T = (size_t)s.T, k = (size_t)s.top_k, E = (size_t)s.E;
   const size_t H = (size_t)s.H, I = (size_t)s.I, P = T * k;
   L.nchunks = (int)((T + kChunk - 1) / kChunk);
-  L.max_mtiles = mtile_bound(s, kStreamBM);  // the larger of the two variants' bounds
+  // the largest bound of the tile heights any variant uses
+  L.max_mtiles = std::max(mtile_bound(s, kStreamBM), mtile_bound(s, kMixedBM));
   L.z = take(T * E * 4);
   L.idx = take(P * 4);
   L.w = take(P * 4);
@@ -438,7 +440,7 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
   int32_t* idx = topk_idx_out ? topk_idx_out : B.idx;
   float* w = topk_w_out ? topk_w_out : B.w;
   const int k = s.top_k;
-  const int BM = use_stream_gemm(s) ? kStreamBM : (s.w_packed ? wide_bm(s) : kTiledBM);
+  const int BM = forward_list_bm(s);
   if (shard) {
     // weights, and fp8 / MXFP4 scales, of experts e0 .. e1 - 1 only
     const size_t ih = (size_t)s.I * s.H;

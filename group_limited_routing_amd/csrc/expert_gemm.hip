@@ -1258,48 +1258,55 @@ __device__ __forceinline__ void backward_epilogue(const GemmArgs& p, const TileI
 
 // ---------------------------------------------------------------- fp8 DMA variant
 // Prefill with packed E4M3 weights and E4M3 A (x or h codes, per-row scales
-// applied in the epilogue). Same tiles, wave grid and tile order as the bf16
-// DMA variant; one matrix-core step is 128 k (16x16x128 fp8), loaded as two
-// half-stages of 64 k: A is BM rows x 64 bytes (chunk g of row r at position
-// g ^ ((r >> 1) & 3)), B is the first or second KB of each of the 16 row
-// blocks' 2 KB fragment blocks (lanes 0-31 of a fragment hold k 0..63, lanes
-// 32-63 k 64..127). The ring has NS half-stage slots and is filled NS - 2
-// half-stages ahead, so the two halves being read are never refilled: the
-// slot refilled at half-stage i last held half-stage i - 2, read by the step
-// that ended before barrier i. Lanes 0-31 read their operands from the
-// step's first half, lanes 32-63 from its second.
-template <int MODE, int BM>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_dma8_kernel(GemmArgs p) {
-  constexpr int A_BYTES = BM * 64, B_BYTES = 16 * 1024, STAGE = A_BYTES + B_BYTES;
-  constexpr int NS = (160 * 1024) / STAGE;     // 5 (BM 256) or 6 (BM 128) slots
-  constexpr int AHEAD = NS - 2;
-  constexpr int FM = BM / 32, FN = 4;
-  constexpr int COLS = (MODE == 0) ? 128 : 256;
-  constexpr int AI = BM / 128;                 // A DMA instructions per wave per half-stage
+// applied in the epilogue). One matrix-core step is 128 k (16x16x128 fp8),
+// loaded as two half-stages of 64 k: A is TM rows x 64 bytes (chunk g of row
+// r at position g ^ ((r >> 1) & 3)), B is the first or second KB of each of
+// the tile's 16-row weight blocks' 2 KB fragment blocks (lanes 0-31 of a
+// fragment hold k 0..63, lanes 32-63 k 64..127). The ring has NS half-stage
+// slots and is filled NS - 2 half-stages ahead, so the two halves being read
+// are never refilled: the slot refilled at half-stage i last held half-stage
+// i - 2, read by the step that ended before barrier i. Lanes 0-31 read their
+// operands from the step's first half, lanes 32-63 from its second.
+//
+// Tile shapes (8 waves, each 16 FM rows x 4 weight blocks, FM = 8 or 4):
+//   TM = 128 or 256: 2 x 4 waves over 16 weight blocks (gate/up: 128 output
+//     columns, 8 gate + 8 up blocks; down: 256 columns);
+//   TM = 512: 4 x 2 waves over 8 weight blocks (gate/up: 64 columns; down:
+//     128), for experts with more than 256 rows: the tile holds all of such
+//     an expert's rows up to 512, so its weights stream from HBM once instead
+//     of once per 256-row tile.
+template <int MODE, int TM>
+struct Dma8Shape {
+  static constexpr int WM = TM >= 512 ? 4 : 2;   // waves along the rows
+  static constexpr int WN = 8 / WM;              // waves along the weight blocks
+  static constexpr int RB = 4 * WN;              // 16-row weight blocks of the tile
+  static constexpr int RW = TM / WM;             // rows of one wave
+  static constexpr int FM = RW / 16, FN = 4;
+  static constexpr int COLS = (MODE == 0) ? RB * 8 : RB * 16;  // output columns
+  static constexpr int A_BYTES = TM * 64, B_BYTES = RB * 1024, STAGE = A_BYTES + B_BYTES;
+  static constexpr int NS = (160 * 1024) / STAGE;  // 6 (TM 128), 5 (256) or 4 (512) slots
+  static constexpr int AHEAD = NS - 2;
+  static constexpr int AI = TM / 128;              // A DMA instructions per wave per half-stage
+  static constexpr int BI = RB / 8;                // B DMA instructions per wave per half-stage
   static_assert(AHEAD >= 2, "ring too small");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+};
 
-  const int ntn = p.N / COLS;
-  const int n_tiles = p.meta[0] * ntn;
-  const int b = blockIdx.x;
-  if (b >= n_tiles) return;
-  const int j = xcd_chunked_tile(b, n_tiles);
-  const int e = p.tile_e[j / ntn];
-  const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
-  const int jj = j - ts * ntn;
-  const int mb = jj / (kGroupM * ntn), rem = jj - mb * kGroupM * ntn;
-  const int gm = min(kGroupM, nm - mb * kGroupM);
-  const int nt = rem / gm, mt = ts + mb * kGroupM + rem % gm;
-  TileInfo ti;
-  ti.e = e;
-  ti.row0 = p.tile_r[mt];
-  ti.rows = min(BM, p.offsets[e + 1] - ti.row0);
+constexpr int kDma8Lds = 160 * 1024;
+
+// One (M-tile, N-tile) of the fp8 DMA GEMM: rows ti.row0 .. + ti.rows of
+// expert ti.e (at most TM), output columns nt * COLS ...
+template <int MODE, int TM>
+__device__ __forceinline__ void dma8_tile(const GemmArgs& p, const TileInfo& ti, int nt,
+                                          uint8_t* smem) {
+  using S = Dma8Shape<MODE, TM>;
+  constexpr int NS = S::NS, AHEAD = S::AHEAD, STAGE = S::STAGE, A_BYTES = S::A_BYTES;
+  constexpr int FM = S::FM, FN = S::FN, AI = S::AI, BI = S::BI, RB = S::RB, RW = S::RW;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3, r = lane & 15, g = lane >> 4;
+  const int wm = wave / S::WN, wn = wave % S::WN, r = lane & 15, g = lane >> 4;
   const int K = p.K, N = p.N;
-  const int n0 = nt * COLS;
+  const int n0 = nt * S::COLS;
 
   // A: instruction i of this wave fills tile rows 16 * (wave * AI + i) ..;
   // lane l writes row l / 4, position l % 4 (chunk (l % 4) ^ ((row >> 1) & 3)).
@@ -1313,25 +1320,27 @@ void gemm_dma8_kernel(GemmArgs p) {
                                       : (const uint8_t*)p.a + (size_t)(ti.row0 + ar) * K;
     asrc[i] = base + chunk * 16;
   }
-  // B: instruction i fills row block wave * 2 + i (MODE 0: 0..7 gate, 8..15 up).
-  const uint8_t* bsrc[2];
+  // B: instruction i fills weight block wave * BI + i (MODE 0: the first RB / 2
+  // blocks gate, the others up).
+  const uint8_t* bsrc[BI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rbk = wave * 2 + i;
-    const uint8_t* W = (const uint8_t*)((MODE == 0 && rbk >= 8) ? p.w1 : p.w0);
-    const int blk = (MODE == 0) ? (n0 >> 4) + (rbk & 7) : (n0 >> 4) + rbk;
+  for (int i = 0; i < BI; ++i) {
+    const int rbk = wave * BI + i;
+    const uint8_t* W = (const uint8_t*)((MODE == 0 && rbk >= RB / 2) ? p.w1 : p.w0);
+    const int blk = (MODE == 0) ? (n0 >> 4) + rbk % (RB / 2) : (n0 >> 4) + rbk;
     bsrc[i] = W + (size_t)ti.e * N * K + (size_t)blk * 16 * K + lane * 16;
   }
   // half-stage hs (k bytes [64 hs, 64 hs + 64)): this wave's first AL row
-  // groups of A (the rest lie past the expert's last row) and two weight blocks
+  // groups of A (the rest lie past the expert's last row) and its weight blocks
   auto issue = [&](int hs, auto al_c) {
     constexpr int AL = decltype(al_c)::value;
     uint8_t* st = smem + (hs % NS) * STAGE;
 #pragma unroll
     for (int i = 0; i < AL; ++i) dma16(asrc[i] + (size_t)hs * 64, st + (wave * AI + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16(bsrc[i] + (size_t)(hs >> 1) * 2048 + (hs & 1) * 1024, st + A_BYTES + (wave * 2 + i) * 1024);
+    for (int i = 0; i < BI; ++i)
+      dma16(bsrc[i] + (size_t)(hs >> 1) * 2048 + (hs & 1) * 1024,
+            st + A_BYTES + (wave * BI + i) * 1024);
   };
 
   // Operand offsets inside a slot; this lane's half of the step is lane / 32.
@@ -1339,12 +1348,12 @@ void gemm_dma8_kernel(GemmArgs p) {
   int aoff[FM], boff[FN];
 #pragma unroll
   for (int f = 0; f < FM; ++f) {
-    const int row = wm * (BM / 2) + f * 16 + r;
+    const int row = wm * RW + f * 16 + r;
     aoff[f] = row * 64 + ((c0 ^ ((row >> 1) & 3)) << 4);
   }
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
-    const int rbl = (MODE == 0) ? ((f < 2) ? wn * 2 + f : 8 + wn * 2 + (f - 2)) : wn * 4 + f;
+    const int rbl = (MODE == 0) ? ((f < 2) ? wn * 2 + f : RB / 2 + wn * 2 + (f - 2)) : wn * 4 + f;
     boff[f] = A_BYTES + rbl * 1024 + (lane & 31) * 32;
   }
   // the second chunk of a row's 32 bytes sits at position (c0 + 1) ^ swizzle,
@@ -1358,7 +1367,7 @@ void gemm_dma8_kernel(GemmArgs p) {
   const int nh = K / 64;  // even, >= 2
   auto kloop = [&](auto nf_c, auto al_c) {
     constexpr int NF = decltype(nf_c)::value;
-    constexpr int PER = decltype(al_c)::value + 2;  // this wave's DMAs per half-stage
+    constexpr int PER = decltype(al_c)::value + BI;  // this wave's DMAs per half-stage
 #pragma unroll
     for (int s0 = 0; s0 < AHEAD; ++s0)
       if (s0 < nh) issue(s0, al_c);
@@ -1406,7 +1415,7 @@ void gemm_dma8_kernel(GemmArgs p) {
       asm volatile("" ::: "memory");
     }
   };
-  const int need = min(FM, max(0, (ti.rows - wm * (BM / 2) + 15) >> 4));
+  const int need = min(FM, max(0, (ti.rows - wm * RW + 15) >> 4));
   const int al = min(AI, max(0, (ti.rows - wave * AI * 16 + 15) >> 4));
   auto run = [&](auto nf_c) {
     if (al == 0)
@@ -1425,7 +1434,68 @@ void gemm_dma8_kernel(GemmArgs p) {
   else
     run(std::integral_constant<int, FM>{});
 
-  transposed_epilogue<MODE, true, FM, FN>(p, ti, acc, wm * (BM / 2), n0, wn, r, g);
+  transposed_epilogue<MODE, true, FM, FN>(p, ti, acc, wm * RW, n0, wn, r, g);
+}
+
+// Every expert in tiles of BM rows (the tile list was built with BM).
+template <int MODE, int BM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_dma8_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDma8Lds];
+  const int ntn = p.N / Dma8Shape<MODE, BM>::COLS;
+  const int n_tiles = p.meta[0] * ntn;
+  const int b = blockIdx.x;
+  if (b >= n_tiles) return;
+  const int j = xcd_chunked_tile(b, n_tiles);
+  const int e = p.tile_e[j / ntn];
+  const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
+  const int jj = j - ts * ntn;
+  const int mb = jj / (kGroupM * ntn), rem = jj - mb * kGroupM * ntn;
+  const int gm = min(kGroupM, nm - mb * kGroupM);
+  const int nt = rem / gm, mt = ts + mb * kGroupM + rem % gm;
+  TileInfo ti;
+  ti.e = e;
+  ti.row0 = p.tile_r[mt];
+  ti.rows = min(BM, p.offsets[e + 1] - ti.row0);
+  dma8_tile<MODE, BM>(p, ti, nt, smem);
+}
+
+// Mixed tile heights (the tile list was built with kMixedBM): an expert with
+// up to 256 rows runs 256-row tiles of COLS(256) columns; an expert with more
+// runs 512-row tiles (two list slots each) of COLS(256) / 2 columns, twice as
+// many of them, so every expert has (slots x N / COLS(256)) units and unit j
+// belongs to slot j / (N / COLS(256)) as with uniform tiles. Inside an
+// expert: blocks of kGroupM (256) or kGroupM / 2 (512) M-tiles, N-tile-major
+// inside a block.
+template <int MODE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_dma8_mixed_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDma8Lds];
+  const int ntn = p.N / Dma8Shape<MODE, 256>::COLS;
+  const int n_tiles = p.meta[0] * ntn;
+  const int b = blockIdx.x;
+  if (b >= n_tiles) return;
+  const int j = xcd_chunked_tile(b, n_tiles);
+  const int e = p.tile_e[j / ntn];
+  const int ts = p.e_tstart[e], nm = p.e_ntiles[e];
+  const int jj = j - ts * ntn;
+  const int end = p.offsets[e + 1];
+  TileInfo ti;
+  ti.e = e;
+  if (end - p.offsets[e] > 256) {
+    constexpr int G = kGroupM / 2;
+    const int nm2 = nm >> 1, ntn2 = 2 * ntn;
+    const int mb = jj / (G * ntn2), rem = jj - mb * G * ntn2;
+    const int gm = min(G, nm2 - mb * G);
+    const int nt = rem / gm, m2 = mb * G + rem % gm;
+    ti.row0 = p.tile_r[ts + 2 * m2];
+    ti.rows = min(512, end - ti.row0);
+    dma8_tile<MODE, 512>(p, ti, nt, smem);
+  } else {
+    ti.row0 = p.tile_r[ts];
+    ti.rows = end - ti.row0;
+    dma8_tile<MODE, 256>(p, ti, jj, smem);
+  }
 }
 
 // ---------------------------------------------------------------- MXFP4 DMA variant
@@ -1641,6 +1711,8 @@ void gemm_dma4_kernel(GemmArgs p) {
 int mtile_bound(const Shape& s, int BM) {
   const long long pairs = (long long)s.T * s.top_k;
   const long long active = pairs < s.E ? pairs : s.E;
+  // mixed heights: 256-row slots, at most two more per expert than its rows need
+  if (BM == kMixedBM) return (int)(2 * active + pairs / 256 + 1);
   return (int)(active + pairs / BM + 1);
 }
 
@@ -1681,10 +1753,22 @@ int wide_bm(const Shape& s) {
   // variants (bf16 tokens, or fp8 weights) skip the matrix-core work of
   // fragments without live rows, so they take 256-row tiles once experts
   // average 96 rows; the register-staged variant (fp32 tokens, bf16 weights)
-  // computes whole tiles and switches at 192.
+  // computes whole tiles and switches at 192. With a hidden size that is not
+  // a multiple of 256 the down pass runs the 128-row tiled kernel (256-column
+  // tiles do not divide it), and both passes walk one tile list: 128 rows.
   const long long pairs = (long long)s.T * s.top_k;
   const bool dma = s.w_fp8 || !s.x_f32;
+  if (s.H % 256 != 0) return 128;
   return pairs >= (dma ? 96LL : 192LL) * s.E ? 256 : 128;
+}
+
+int forward_list_bm(const Shape& s) {
+  if (use_stream_gemm(s)) return kStreamBM;
+  if (!s.w_packed) return kTiledBM;
+  const int bm = wide_bm(s);
+  // packed fp8 weights at 256-row tiles: 512-row tiles for experts beyond 256 rows
+  if (bm == 256 && s.w_fp8 && !s.w_mx4) return kMixedBM;
+  return bm;
 }
 
 template <int MODE, typename AT, bool FP8, int BM>
@@ -1703,7 +1787,17 @@ static void launch_wide_bm(const Shape& s, const GemmArgs& g, hipStream_t st) {
 
 template <int MODE, typename AT, bool FP8>
 static void launch_wide(const Shape& s, const GemmArgs& g, hipStream_t st) {
-  if (wide_bm(s) == 256)
+  const int lbm = forward_list_bm(s);
+  if constexpr (FP8) {
+    if (lbm == kMixedBM) {
+      // one unit per (256-row slot, 256-row-tile N-tile); surplus units exit
+      long long n = (long long)mtile_bound(s, kMixedBM) * (g.N / Dma8Shape<MODE, 256>::COLS);
+      n = (n + 7) & ~7LL;
+      gemm_dma8_mixed_kernel<MODE><<<(unsigned)n, 512, 0, st>>>(g);
+      return;
+    }
+  }
+  if (lbm == 256)
     launch_wide_bm<MODE, AT, FP8, 256>(s, g, st);
   else
     launch_wide_bm<MODE, AT, FP8, 128>(s, g, st);

@@ -12,6 +12,9 @@ namespace beam {
 // Row tile (tokens per M-tile) of the two expert-GEMM variants.
 constexpr int kStreamBM = 16;   // decode: weight streaming, one MFMA row block
 constexpr int kTiledBM = 128;   // prefill, row-major weights: LDS-staged MFMA tiles
+// M-tile list of the mixed-height DMA GEMMs: 256-row slots, and 512-row tiles
+// (two slots each) for experts with more than 256 rows.
+constexpr int kMixedBM = 512;
 
 struct Shape {
   int T, H, I, E, n_group, topk_group, top_k;
@@ -41,6 +44,10 @@ Layout make_layout(const Shape& s);
 bool use_stream_gemm(const Shape& s);
 // prefill with packed weights: M-tile of 128 or 256 rows, from the rows per expert
 int wide_bm(const Shape& s);
+// Row height of the forward's M-tile list (shared by the gate/up and down
+// passes): kStreamBM, kTiledBM, 128, 256, or kMixedBM (256-row slots, 512-row
+// tiles for experts with more than 256 rows).
+int forward_list_bm(const Shape& s);
 int mtile_bound(const Shape& s, int BM);
 
 hipError_t launch_router_logits(const void* x, int x_f32, const float* W, float* z, int T, int H,

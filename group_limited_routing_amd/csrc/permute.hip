@@ -44,6 +44,17 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
   chist[(size_t)blockIdx.x * kExperts + e] = cnt;
 }
 
+// M-tile slots of an expert with n rows. BM rows per slot; with
+// BM == kMixedBM the slots hold 256 rows and an expert with more than 256
+// rows takes 512-row tiles, two slots each (so its count is even and the
+// first slot of each pair starts the tile).
+__device__ __forceinline__ int expert_slots(int n, int BM) {
+  if (BM != kMixedBM) return (n + BM - 1) / BM;
+  return n > 256 ? 2 * ((n + 511) / 512) : (n + 255) / 256;
+}
+
+__device__ __forceinline__ int slot_rows(int BM) { return BM == kMixedBM ? 256 : BM; }
+
 // Exclusive prefix sum over the 256 threads of the block.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -64,7 +75,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
 // One workgroup, thread e = expert e:
 //   cbase[c, e]  = tokens of expert e in chunks before c;
 //   counts[e]    = tokens of expert e; offsets = exclusive scan of counts;
-//   M-tiles of BM rows per expert, listed expert by expert:
+//   M-tiles of BM rows per expert (expert_slots), listed expert by expert:
 //   tile_e[m] = expert, tile_r[m] = first sorted row; meta[0] = tile count;
 //   e_tstart[e], e_ntiles[e] = first M-tile of expert e and its tile count.
 __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restrict__ chist,
@@ -92,13 +103,14 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restric
   offsets[e] = off;
   if (e == kExperts - 1) offsets[kExperts] = off + run;
   // experts outside [e0, e1) keep their place in the sorted order but get no tiles
-  const int mt = (e >= e0 && e < e1) ? (run + BM - 1) / BM : 0;
+  const int mt = (e >= e0 && e < e1) ? expert_slots(run, BM) : 0;
   const int ts = block_exclusive_scan(mt, wsum);
   e_tstart[e] = ts;
   e_ntiles[e] = mt;
+  const int sr = slot_rows(BM);
   for (int i = 0; i < mt; ++i) {
     tile_e[ts + i] = e;
-    tile_r[ts + i] = off + i * BM;
+    tile_r[ts + i] = off + i * sr;
   }
   if (e == kExperts - 1) meta[0] = ts + mt;
 }
@@ -219,13 +231,14 @@ __global__ __launch_bounds__(256) void perm_single_kernel(
   const int off = block_exclusive_scan(run, wsum);
   offsets[e] = off;
   if (e == kExperts - 1) offsets[kExperts] = off + run;
-  const int mt = (e >= e0 && e < e1) ? (run + BM - 1) / BM : 0;
+  const int mt = (e >= e0 && e < e1) ? expert_slots(run, BM) : 0;
   const int ts = block_exclusive_scan(mt, wsum);
   e_tstart[e] = ts;
   e_ntiles[e] = mt;
+  const int sr = slot_rows(BM);
   for (int i = 0; i < mt; ++i) {
     tile_e[ts + i] = e;
-    tile_r[ts + i] = off + i * BM;
+    tile_r[ts + i] = off + i * sr;
   }
   if (e == kExperts - 1) meta[0] = ts + mt;
   eoff[e] = off;

@@ -141,6 +141,24 @@ def test_fp8_dma_variant_256_rows():
     _full_compare("fp8 dma 256", cfg, 16, True)
 
 
+def test_fp8_mixed_tile_heights():
+    # about 256 rows per expert (as at the fp8 workload's T = 8192): experts
+    # beyond 256 rows run 512-row tiles, the others 256-row tiles, in one launch
+    cfg = _case(8192, 256, 256, w_dtype="fp8")
+    out, r = _full_compare("fp8 mixed tiles", cfg, 27, True)
+    cnt = r["expert_counts"].cpu().numpy()
+    assert (cnt > 256).sum() >= 32 and (cnt <= 256).sum() >= 32, cnt
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
+def test_hidden_not_a_multiple_of_256_at_many_rows(w_dtype):
+    # packed weights, about 100 rows per expert, hidden 384: the down pass
+    # runs the 128-row tiled kernel (256-column tiles do not divide 384), so
+    # the shared tile list must hold 128-row tiles for both passes
+    cfg = _case(3200, 384, 256, w_dtype=w_dtype)
+    _full_compare(f"hidden 384 packed {w_dtype}", cfg, 28, True)
+
+
 @pytest.mark.parametrize("T", [255, 256, 257, 512])
 def test_routing_paths_at_the_single_chunk_boundary(T):
     # up to 256 tokens: split-K fp32 router logits and the one-launch

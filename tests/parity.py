@@ -45,16 +45,60 @@ def packed_copy(w):
     return pw
 
 
+GUARD = 4096       # canary bytes before and after a guarded buffer
+CANARY = 0xA5
+
+
+class Guarded:
+    """nbytes of device memory with GUARD canary bytes on both sides. The
+    library is handed ``view`` (256-byte aligned) and told its exact size;
+    ``check()`` after the call asserts that no byte outside it changed."""
+
+    def __init__(self, nbytes, device, what):
+        self.n, self.what = int(nbytes), what
+        self.full = torch.full((self.n + 2 * GUARD,), CANARY, dtype=torch.uint8, device=device)
+        self.view = self.full[GUARD:GUARD + self.n]
+
+    def tensor(self, shape, dtype):
+        return self.view.view(dtype).view(shape)
+
+    def check(self):
+        if self.full.is_cuda:
+            torch.cuda.synchronize()
+        head, tail = self.full[:GUARD], self.full[GUARD + self.n:]
+        assert bool((head == CANARY).all()), f"{self.what}: bytes written before its start"
+        assert bool((tail == CANARY).all()), f"{self.what}: bytes written past its end"
+
+
+def guarded_workspace(x, w, cfg):
+    """A guarded workspace of exactly the size the library asks for."""
+    c = gl.make_config(x.shape[1], w["w_gate"].shape[1], cfg["n_experts"], cfg["n_group"],
+                       cfg["topk_group"], cfg["top_k"], cfg["routed_scaling_factor"], x.dtype,
+                       w["w_gate"].dtype, w.get("packed", False))
+    return Guarded(gl.workspace_bytes(c, x.shape[0]), x.device, "workspace")
+
+
+def guarded_out(x):
+    g = Guarded(x.numel() * x.element_size(), x.device, "out")
+    return g, g.tensor(tuple(x.shape), x.dtype)
+
+
 def run_forward(x, rw, b, w, cfg, **kw):
+    """beam_moe_forward with routing outputs, on a guarded workspace and a
+    guarded output buffer (checked after the call)."""
     scales = None
     if w["w_gate"].dtype in (torch.float8_e4m3fn, torch.uint8):
         scales = (w["w_gate_scale"], w["w_up_scale"], w["w_down_scale"])
+    ws = guarded_workspace(x, w, cfg)
+    og, out = guarded_out(x)
     out, r = gl.forward(x, rw, b, w["w_gate"], w["w_up"], w["w_down"], scales=scales,
                         packed=w.get("packed", False),
                         n_group=cfg["n_group"], topk_group=cfg["topk_group"], top_k=cfg["top_k"],
                         routed_scaling_factor=cfg["routed_scaling_factor"], return_routing=True,
-                        return_logits=True, **kw)
+                        return_logits=True, workspace=ws.view, out=out, **kw)
     torch.cuda.synchronize()
+    ws.check()
+    og.check()
     return out, r
 
 

@@ -16,7 +16,8 @@ import torch
 import oracle
 import workloads
 import group_limited_routing_amd as gl
-from parity import check_routing, coverage_report, expert_getter, output_errors, tile_cover
+from parity import (Guarded, check_routing, coverage_report, expert_getter, output_errors,
+                    tile_cover)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,11 +61,18 @@ def _packed(w):
 
 
 def _run(cfg, x, rw, b, pw, dout, weight_grads=True):
+    """beam_moe_backward on a guarded workspace of exactly the size it asks for."""
+    c = gl.make_config(x.shape[1], pw["w_gate"].shape[1], cfg["n_experts"], cfg["n_group"],
+                       cfg["topk_group"], cfg["top_k"], cfg["routed_scaling_factor"],
+                       torch.bfloat16, torch.bfloat16, packed=True)
+    ws = Guarded(gl.backward_workspace_bytes(c, x.shape[0], weight_grads), x.device,
+                 "backward workspace")
     g = gl.backward(x, rw, b, pw["w_gate"], pw["w_up"], pw["w_gate_t"], pw["w_up_t"],
                     pw["w_down_t"], dout, weight_grads=weight_grads, n_group=cfg["n_group"],
                     topk_group=cfg["topk_group"], top_k=cfg["top_k"],
-                    routed_scaling_factor=cfg["routed_scaling_factor"])
+                    routed_scaling_factor=cfg["routed_scaling_factor"], workspace=ws.view)
     torch.cuda.synchronize()
+    ws.check()
     return g
 
 

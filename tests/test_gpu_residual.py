@@ -17,7 +17,8 @@ import torch
 import oracle
 import workloads
 import group_limited_routing_amd as gl
-from parity import check_outputs, check_routing, oracle_reference, packed_copy
+from parity import (check_outputs, check_routing, guarded_out, guarded_workspace,
+                    oracle_reference, packed_copy)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,11 +51,15 @@ def _run(name, cfg, seed, step, eps=1e-6, packed=False, in_place=False, tokens=N
     stream64 = stream.cpu().double().numpy()
     print(f"\n[residual] {name}: T={cfg['T']} H={cfg['hidden']} I={cfg['intermediate']} "
           f"step={step} eps={eps}", flush=True)
+    ws = guarded_workspace(x, gw, cfg)
+    og, gout = guarded_out(x)
     out, r = gl.forward_residual(x, rw, b, gw["w_gate"], gw["w_up"], gw["w_down"], stream, gain,
                                  step, norm_eps=eps, scales=_scales(gw),
-                                 packed=gw.get("packed", False), out=stream if in_place else None,
-                                 return_routing=True)
+                                 packed=gw.get("packed", False), out=stream if in_place else gout,
+                                 return_routing=True, workspace=ws.view)
     torch.cuda.synchronize()
+    ws.check()
+    og.check()
     if in_place:
         assert out.data_ptr() == stream.data_ptr()
     T = cfg["T"]

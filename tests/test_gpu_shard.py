@@ -14,8 +14,8 @@ import torch
 import oracle
 import workloads
 import group_limited_routing_amd as gl
-from parity import (check_outputs, check_routing, expert_getter, oracle_reference, packed_copy,
-                    run_forward)
+from parity import (check_outputs, check_routing, expert_getter, guarded_out, guarded_workspace,
+                    oracle_reference, packed_copy, run_forward)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,13 +44,17 @@ def _shard_forward(x, rw, b, w, cfg, e0, e1):
     scales = None
     if sw["w_gate"].dtype in (torch.float8_e4m3fn, torch.uint8):
         scales = (sw["w_gate_scale"], sw["w_up_scale"], sw["w_down_scale"])
+    ws = guarded_workspace(x, sw, cfg)
+    og, out = guarded_out(x)
     out, r = gl.forward_shard(x, rw, b, e0, e1, sw["w_gate"], sw["w_up"], sw["w_down"],
                               scales=scales, packed=sw.get("packed", False),
                               n_group=cfg["n_group"], topk_group=cfg["topk_group"],
                               top_k=cfg["top_k"],
                               routed_scaling_factor=cfg["routed_scaling_factor"],
-                              return_routing=True)
+                              return_routing=True, workspace=ws.view, out=out)
     torch.cuda.synchronize()
+    ws.check()
+    og.check()
     return out, r
 
 

@@ -3,10 +3,12 @@ routing, the M-tile coverage of a token sample, and the decode tables that
 stand in for the oracle's per-weight decoders."""
 
 import numpy as np
+import pytest
+import torch
 
 import oracle
-from parity import (coverage_report, e4m3_dequantize, expert_rows, mx_dequantize, tile_cover,
-                    tiles_covered)
+from parity import (GUARD, Guarded, coverage_report, e4m3_dequantize, expert_rows, mx_dequantize,
+                    tile_cover, tiles_covered)
 
 
 def _routing(T, E=256, k=8, hot=(), seed=0):
@@ -70,3 +72,17 @@ def test_decode_tables_equal_the_oracle_decoders():
     packed = rng.integers(0, 256, size=(32, 256), dtype=np.uint8)
     scales = rng.integers(100, 150, size=(32, 16), dtype=np.uint8)
     assert np.array_equal(mx_dequantize(packed, scales), oracle.mxfp4.dequantize(packed, scales))
+
+
+def test_guarded_buffer_catches_writes_outside_it():
+    g = Guarded(1000, "cpu", "ws")
+    assert g.view.numel() == 1000 and g.view.data_ptr() % 256 == g.full.data_ptr() % 256
+    g.view.fill_(7)  # anything inside is fine
+    g.check()
+    for where in (GUARD - 1, GUARD + 1000):
+        h = Guarded(1000, "cpu", "ws")
+        h.full[where] = 0
+        with pytest.raises(AssertionError):
+            h.check()
+    t = Guarded(8 * 6 * 2, "cpu", "out").tensor((8, 6), torch.bfloat16)
+    assert t.shape == (8, 6) and t.dtype == torch.bfloat16

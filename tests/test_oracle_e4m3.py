@@ -82,3 +82,47 @@ def test_quantize_rows():
         err = np.abs(deq[r] - v[r])
         bound = np.maximum(np.abs(v[r]) * 2.0 ** -4, 2.0 ** -10 * scale[r]) * 1.0001
         assert np.all(err <= bound)
+
+
+def _rows_where_the_readings_differ(rng, n_rows):
+    """Rows [amax, v] (amax the row's largest magnitude) with v within a few
+    fp32 ulps of where an E4M3 rounding boundary falls, found by search."""
+    mids = (e4m3.decode(np.arange(0, 0x7E, dtype=np.uint8)) +
+            e4m3.decode(np.arange(1, 0x7F, dtype=np.uint8))) / 2
+    rows = []
+    while len(rows) < n_rows:
+        amax = np.float32(np.exp(rng.uniform(-4, 4)))
+        inv = np.float32(448.0) / amax
+        scale = amax / np.float32(448.0)
+        m = mids[rng.integers(8, len(mids))]
+        v0 = np.float32(m / np.float64(inv))
+        for k in range(-8, 9):
+            v = np.float32(v0 + np.float32(k) * np.spacing(v0))
+            if not 0 < v < amax:
+                continue
+            p1, p2 = np.float32(v * inv), np.float32(v / scale)
+            if (p1 - m) * (p2 - m) <= 0 and p1 != p2:
+                rows.append([amax, v])
+                break
+    return np.array(rows, dtype=np.float32)
+
+
+def test_quantize_rows_multiplies_by_the_fp32_reciprocal():
+    """The row reading: codes = e4m3(fp32(v * fp32(448 / amax))), the same
+    correctly rounded fp32 steps the GPU takes. Dividing by the stored scale
+    fp32(amax / 448) is a plausible other reading that rounds differently
+    near code boundaries; on rows built to sit there, the oracle must give
+    the multiply path's codes. Both paths are computed with torch's float32
+    arithmetic and torch's float8_e4m3fn cast, independently of the oracle's
+    own encoder, and they do disagree on these rows."""
+    v = _rows_where_the_readings_differ(np.random.default_rng(7), 64)
+    t = torch.from_numpy(v)
+    amax = t.abs().amax(dim=1)
+    inv = torch.tensor(448.0, dtype=torch.float32) / amax
+    scale = amax / torch.tensor(448.0, dtype=torch.float32)
+    mul = (t * inv[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    div = (t / scale[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (mul != div).any(axis=1).sum() >= 32   # the readings really differ here
+    codes, sc = e4m3.quantize_rows(v)
+    assert np.array_equal(codes, mul)
+    assert np.array_equal(sc, scale.numpy())

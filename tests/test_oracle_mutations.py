@@ -145,3 +145,19 @@ def test_backward_sigmoid_slope_dropped_is_caught(monkeypatch):
     monkeypatch.setattr(ob, "backward", no_slope)
     assert _fails(tb.test_finite_differences_every_parameter)
     assert _fails(tb.test_matches_torch_autograd, 2)
+
+
+def test_row_quantiser_dividing_by_the_scale_is_caught(monkeypatch):
+    """Quantising a row as e4m3(v / fp32(amax / 448)) instead of
+    e4m3(v * fp32(448 / amax))."""
+    def quantize_rows_div(v):
+        v32 = np.asarray(v, dtype=np.float32)
+        amax = np.max(np.abs(v32), axis=1)
+        zero = amax == 0
+        safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
+        scale = (safe / np.float32(e4m3.FP8_MAX)).astype(np.float32)
+        codes = e4m3.encode((v32 / scale[:, None]).astype(np.float32).astype(np.float64))
+        codes[zero, :] = 0
+        return codes, np.where(zero, np.float32(1.0), scale).astype(np.float32)
+    monkeypatch.setattr(e4m3, "quantize_rows", quantize_rows_div)
+    assert _fails(te.test_quantize_rows_multiplies_by_the_fp32_reciprocal)

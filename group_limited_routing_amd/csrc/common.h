@@ -111,6 +111,19 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
 #endif
 }
 
+// The same with the non-temporal cache policy (the NT bit): for weights
+// that each workgroup streams once, so they do not displace reused lines.
+__device__ __forceinline__ void dma16_nt(const void* gsrc, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 2);
+#endif
+}
+
+// 16 bytes from global memory with the non-temporal hint (streamed weights).
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // Wait until at most N vector-memory operations of this wave are pending
 // (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and
 // lgkmcnt left unconstrained).

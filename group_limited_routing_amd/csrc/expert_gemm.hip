@@ -84,6 +84,19 @@ __device__ __forceinline__ OpReg<FP8> load_op(const void* p) {
   }
 }
 
+// A weight operand: read once per workgroup, so loaded non-temporally.
+template <bool FP8>
+__device__ __forceinline__ OpReg<FP8> load_w(const void* p) {
+  if constexpr (FP8) {
+    Op32 o;
+    o.lo = ld16_nt(p);
+    o.hi = ld16_nt((const uint8_t*)p + 16);
+    return o;
+  } else {
+    return ld16_nt(p);
+  }
+}
+
 
 // The A operand of a bf16 pass may be stored as fp32 (x in fp32); it is then
 // rounded to bf16 (nearest even) on load. 8 values per lane.
@@ -240,7 +253,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
     else
       aq16[d].load((const typename std::conditional<FP8, uint16_t, AT>::type*)arow + (size_t)s * KSTEP);
 #pragma unroll
-    for (int f = 0; f < FN; ++f) bq[d][f] = load_op<FP8>(brow[f] + (size_t)s * BSTEP);
+    for (int f = 0; f < FN; ++f) bq[d][f] = load_w<FP8>(brow[f] + (size_t)s * BSTEP);
   };
   auto consume = [&](int d) {
     OR a;
@@ -371,7 +384,7 @@ __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
     aq[d].hi = ld16(arow + (size_t)s * 128 + 64);
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
-      bq[d][f] = ld16(brow[f] + (size_t)s * 1024);
+      bq[d][f] = ld16_nt(brow[f] + (size_t)s * 1024);
       sq[d][f] = srow[f][(s >> 2) * 64] >> (8 * (s & 3));
     }
   };
@@ -1339,8 +1352,8 @@ __device__ __forceinline__ void dma8_tile(const GemmArgs& p, const TileInfo& ti,
     for (int i = 0; i < AL; ++i) dma16(asrc[i] + (size_t)hs * 64, st + (wave * AI + i) * 1024);
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      dma16(bsrc[i] + (size_t)(hs >> 1) * 2048 + (hs & 1) * 1024,
-            st + A_BYTES + (wave * BI + i) * 1024);
+      dma16_nt(bsrc[i] + (size_t)(hs >> 1) * 2048 + (hs & 1) * 1024,
+               st + A_BYTES + (wave * BI + i) * 1024);
   };
 
   // Operand offsets inside a slot; this lane's half of the step is lane / 32.
@@ -1589,7 +1602,7 @@ void gemm_dma4_kernel(GemmArgs p) {
     uint8_t* st = smem + (hs % NS) * STAGE;
 #pragma unroll
     for (int i = 0; i < AL; ++i) dma16(asrc[i] + (size_t)hs * 64, st + (wave * AI + i) * 1024);
-    dma16(bsrc + (size_t)(hs >> 1) * 1024 + (hs & 1) * 512, st + A_BYTES + wave * 1024);
+    dma16_nt(bsrc + (size_t)(hs >> 1) * 1024 + (hs & 1) * 512, st + A_BYTES + wave * 1024);
   };
 
   // Operand offsets: A chunk g of this lane's row (both halves of the step),

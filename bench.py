@@ -95,8 +95,11 @@ def gateup_kernel(cfg):
         return f"gemm_stream_kernel<0, {'unsigned char' if fp8 else xt}, {str(fp8).lower()}, true, ...>"
     dma = fp8 or xt == "unsigned short"
     bm = 256 if pairs >= (96 if dma else 192) * cfg["n_experts"] else 128
+    if cfg["hidden"] % 256:
+        bm = 128
     if fp8:
-        return f"gemm_dma8_kernel<0, {bm}>"
+        # 256-row tiles: mixed heights (512 rows for experts beyond 256)
+        return "gemm_dma8_mixed_kernel<0>" if bm == 256 else f"gemm_dma8_kernel<0, {bm}>"
     if dma:
         return f"gemm_dma_kernel<0, {bm}>"
     return f"gemm_wide_kernel<0, {xt}, false, {bm}>"
@@ -208,7 +211,7 @@ def stored_figure(workload, name="gateup", sources=KERNEL_SOURCES, key="hbm_byte
         v = float(vals[key])
     except (KeyError, ValueError):
         return None
-    return int(v) if key == "hbm_bytes_per_launch" else v
+    return int(v) if key.endswith("hbm_bytes_per_launch") else v
 
 
 class Bench:
@@ -574,7 +577,7 @@ def write_mfma(pmc_dir, workload):
     instructions per dispatch."""
     import re
     rows = _counter_rows(pmc_dir)
-    pat = re.compile(r"beam::gemm_\w+<([01]),")
+    pat = re.compile(r"beam::gemm_\w+<([01])[,>]")
     per = {}
     for r in rows:
         m = pat.search(r["Kernel_Name"])
@@ -637,7 +640,7 @@ def write_wgrad_traffic(fetch_dir, write_dir):
     per_launch = (f["kib"] * f["factor"] + w["kib"] * w["factor"]) * 1024
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d <dir> -o run --output-format csv "
            "-- python3 /root/repo/bench.py --steps 3 --warmup 1 --no-prefill --no-residual "
-           "--no-shard --no-cpu-baseline --calibrate-copy --backward-steps 2")
+           "--no-shard --no-fp8 --no-cpu-baseline --calibrate-copy --backward-steps 2")
     path = os.path.join(ROOT, "profiles", "wgrad_backward_counters.txt")
     with open(path, "w") as fh:
         fh.write("# HBM traffic of the backward's weight-gradient GEMMs (prefill shape, all\n"
@@ -660,45 +663,50 @@ def write_wgrad_traffic(fetch_dir, write_dir):
 def write_traffic(fetch_dir, write_dir, workload):
     """Turn one FETCH_SIZE pass and one WRITE_SIZE pass (rocprofv3 --pmc, KiB per
     dispatch) over `bench.py --workload W --no-prefill --calibrate-copy` into
-    HBM bytes per gate/up launch. Each counter is scaled by what it reads for
-    the 1 GiB device copy made before the timed region (the largest copyBuffer
-    dispatch of the run)."""
+    HBM bytes per launch of the gate/up and of the down GEMM. Each counter is
+    scaled by what it reads for the 1 GiB device copy made before the timed
+    region (the largest copyBuffer dispatch of the run)."""
     import re
-    pat = re.compile(r"beam::gemm_\w+<0,")
+    pats = {"gateup": re.compile(r"beam::gemm_\w+<0[,>]"), "down": re.compile(r"beam::gemm_\w+<1[,>]")}
     out = {}
     for name, d in (("fetch", fetch_dir), ("write", write_dir)):
         rows = _counter_rows(d)
         copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
-        gu = [r for r in rows if pat.search(r["Kernel_Name"])]
-        kernels = sorted({r["Kernel_Name"] for r in gu})
-        if len(kernels) != 1:
-            raise SystemExit(f"expected one gate/up kernel in {d}, found {kernels}")
-        out[name] = {"copy_kib": copy, "factor": COPY_CAL_KIB / copy,
-                     "kib": sum(float(r["Counter_Value"]) for r in gu) / len(gu),
-                     "n": len(gu), "kernel": kernels[0]}
+        out[name] = {"copy_kib": copy, "factor": COPY_CAL_KIB / copy}
+        for stage, pat in pats.items():
+            sel = [r for r in rows if pat.search(r["Kernel_Name"])]
+            kernels = sorted({r["Kernel_Name"] for r in sel})
+            if len(kernels) != 1:
+                raise SystemExit(f"expected one {stage} kernel in {d}, found {kernels}")
+            out[name][stage] = {"kib": sum(float(r["Counter_Value"]) for r in sel) / len(sel),
+                                "n": len(sel), "kernel": kernels[0]}
     f, w = out["fetch"], out["write"]
-    hbm = (f["kib"] * f["factor"] + w["kib"] * w["factor"]) * 1024
+    hbm = {st: (f[st]["kib"] * f["factor"] + w[st]["kib"] * w["factor"]) * 1024 for st in pats}
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --kernel-include-regex 'gemm|copyBuffer' "
            "-d <dir> -o run --output-format csv "
            f"-- python3 /root/repo/bench.py --workload {workload} --steps 3 --warmup 1 --no-prefill "
            "--no-residual --no-backward --no-shard --no-fp8 --no-cpu-baseline --calibrate-copy")
     path = os.path.join(ROOT, "profiles", f"gateup_{workload}_counters.txt")
     with open(path, "w") as fh:
-        fh.write(f"# HBM traffic of the gate/up grouped GEMM, workload {workload}, one MI355X\n")
+        fh.write(f"# HBM traffic of the gate/up and down grouped GEMMs, workload {workload}, one MI355X\n")
         fh.write("# commands (one counter per pass):\n")
         fh.write("#   " + cmd.format(c="FETCH_SIZE") + "\n")
         fh.write("#   " + cmd.format(c="WRITE_SIZE") + "\n")
         fh.write(f"#   python3 bench.py --traffic <fetch dir> <write dir> --workload {workload}\n")
         fh.write("# calibration: a 1 GiB device copy reads and writes 1048576 KiB\n")
-        fh.write(f"kernel = {f['kernel']}\n")
-        fh.write(f"dispatches = {f['n']}\n")
-        fh.write(f"fetch_kib_per_dispatch = {f['kib']:.1f}\n")
-        fh.write(f"write_kib_per_dispatch = {w['kib']:.1f}\n")
+        fh.write(f"kernel = {f['gateup']['kernel']}\n")
+        fh.write(f"dispatches = {f['gateup']['n']}\n")
+        fh.write(f"fetch_kib_per_dispatch = {f['gateup']['kib']:.1f}\n")
+        fh.write(f"write_kib_per_dispatch = {w['gateup']['kib']:.1f}\n")
+        fh.write(f"down_kernel = {f['down']['kernel']}\n")
+        fh.write(f"down_fetch_kib_per_dispatch = {f['down']['kib']:.1f}\n")
+        fh.write(f"down_write_kib_per_dispatch = {w['down']['kib']:.1f}\n")
         fh.write(f"copy_fetch_kib = {f['copy_kib']:.1f}\n")
         fh.write(f"copy_write_kib = {w['copy_kib']:.1f}\n")
         fh.write(f"fetch_factor = {f['factor']:.4f}\n")
         fh.write(f"write_factor = {w['factor']:.4f}\n")
-        fh.write(f"hbm_bytes_per_launch = {hbm:.0f}\n")
+        fh.write(f"hbm_bytes_per_launch = {hbm['gateup']:.0f}\n")
+        fh.write(f"down_hbm_bytes_per_launch = {hbm['down']:.0f}\n")
         fh.write(f"kernel_source_sha = {kernel_source_sha()}\n")
     print(open(path).read())
 
@@ -715,7 +723,8 @@ def workload_line(cfg, bench, steps, warmup):
     lb, lf = layer_work(cfg, bench.active)
     step_s = res["ms_per_step"] / 1e3
     rl = roofline(gb, gf, res["gateup_ms"] / 1e3, wdt, stored_figure(name))
-    drl = roofline(db, df, res["down_ms"] / 1e3, wdt)
+    drl = roofline(db, df, res["down_ms"] / 1e3, wdt,
+                   stored_figure(name, key="down_hbm_bytes_per_launch"))
     return {
         "workload": describe(cfg),
         "value": round(cfg["T"] / step_s, 1), "unit": "tokens/s",

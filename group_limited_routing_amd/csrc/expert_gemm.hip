@@ -1976,7 +1976,8 @@ hipError_t launch_pack(const void* src, void* dst, int E, int rows, int cols, in
 
 // ---------------------------------------------------------------- combine
 // out[t] = sum over slots j (ascending) of y_perm[inv[t, j]], in fp32; the
-// rows already carry rsf * w. One thread per 8 output values.
+// rows already carry rsf * w. One thread per 8 output values. Every y row is
+// read once, so with the non-temporal hint.
 template <int OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ inv, int T,
@@ -1991,7 +1992,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll 4
   for (int j = 0; j < k; ++j) {
     const int pos = inv[(size_t)t * k + j];
-    const u32x4 q = ld16(y + (size_t)pos * H + c * 8);
+    const u32x4 q = ld16_nt(y + (size_t)pos * H + c * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] += bf16_bits_to_f32(q[i] & 0xffffu);
@@ -2053,7 +2054,7 @@ __global__ __launch_bounds__(kResidualThreads) void combine_residual_kernel(
     if (c < vpr) {
 #pragma unroll 4
       for (int j = 0; j < k; ++j) {
-        const u32x4 q = ld16(y + (size_t)slots[j] * H + c * 8);
+        const u32x4 q = ld16_nt(y + (size_t)slots[j] * H + c * 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[u][2 * i] += bf16_bits_to_f32(q[i] & 0xffffu);
@@ -2175,7 +2176,7 @@ __global__ __launch_bounds__(256) void quant_h_kernel(const float* __restrict__ 
   const float amax = __uint_as_float(hamax[row]);
   const float inv = amax > 0.f ? 448.0f / amax : 0.f;
   for (int c = threadIdx.x * 4; c < I; c += 256 * 4) {
-    const u32x4 v = ld16(hf + row * I + c);
+    const u32x4 v = ld16_nt(hf + row * I + c);  // h is read once
     uint32_t w = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w |= f32_to_e4m3(__uint_as_float(v[i]) * inv) << (8 * i);

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void combine_shard_kernel(const uint16_t* __re
   for (int j = 0; j < k; ++j) {
     const int e = idx[(size_t)t * k + j];
     if (e < e0 || e >= e1) continue;
-    const u32x4 q = *reinterpret_cast<const u32x4*>(y + (size_t)inv[(size_t)t * k + j] * H + c * 8);
+    const u32x4 q = ld16_nt(y + (size_t)inv[(size_t)t * k + j] * H + c * 8);  // read once
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] += bf16_bits_to_f32(q[i] & 0xffffu);

@@ -99,12 +99,14 @@ def test_traffic_summary_scales_by_the_copy(sandbox, monkeypatch):
     _write_counters(sandbox / "f", [(1, COPY, "FETCH_SIZE", 524288, 0, 1),
                                     (2, GATEUP, "FETCH_SIZE", 2900, 0, 1),
                                     (3, GATEUP, "FETCH_SIZE", 3100, 0, 1),
-                                    (4, DOWN, "FETCH_SIZE", 99999, 0, 1)])
+                                    (4, DOWN, "FETCH_SIZE", 500, 0, 1)])
     _write_counters(sandbox / "w", [(1, COPY, "WRITE_SIZE", 1048576, 0, 1),
                                     (2, GATEUP, "WRITE_SIZE", 1000, 0, 1),
-                                    (3, GATEUP, "WRITE_SIZE", 1000, 0, 1)])
+                                    (3, GATEUP, "WRITE_SIZE", 1000, 0, 1),
+                                    (4, DOWN, "WRITE_SIZE", 300, 0, 1)])
     bench.write_traffic(str(sandbox / "f"), str(sandbox / "w"), "decode")
     assert bench.stored_figure("decode") == (3000 * 2 + 1000) * 1024
+    assert bench.stored_figure("decode", key="down_hbm_bytes_per_launch") == (500 * 2 + 300) * 1024
     # counters taken on other kernel sources are not used
     monkeypatch.setattr(bench, "kernel_source_sha", lambda paths=None: "fedcba9876543210")
     assert bench.stored_figure("decode") is None
@@ -134,3 +136,51 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_counter_summaries_match_the_mixed_fp8_kernel(sandbox):
+    """The fp8 GEMMs at 256-row tiles are gemm_dma8_mixed_kernel<0> / <1>
+    (no second template argument): the parsers must still tell gate/up from
+    down."""
+    gu = "void beam::gemm_dma8_mixed_kernel<0>(beam::GemmArgs)"
+    dn = "void beam::gemm_dma8_mixed_kernel<1>(beam::GemmArgs)"
+    _write_counters(sandbox / "f", [(1, COPY, "FETCH_SIZE", 524288, 0, 1),
+                                    (2, gu, "FETCH_SIZE", 1000, 0, 1),
+                                    (3, dn, "FETCH_SIZE", 400, 0, 1)])
+    _write_counters(sandbox / "w", [(1, COPY, "WRITE_SIZE", 1048576, 0, 1),
+                                    (2, gu, "WRITE_SIZE", 100, 0, 1),
+                                    (3, dn, "WRITE_SIZE", 50, 0, 1)])
+    bench.write_traffic(str(sandbox / "f"), str(sandbox / "w"), "fp8")
+    assert bench.stored_figure("fp8") == (1000 * 2 + 100) * 1024
+    assert bench.stored_figure("fp8", key="down_hbm_bytes_per_launch") == (400 * 2 + 50) * 1024
+    assert bench.gateup_kernel(workloads.workload("fp8")) == "gemm_dma8_mixed_kernel<0>"
+
+
+def test_every_global_name_main_uses_exists():
+    """bench.main() only runs on a GPU machine; a name it calls that the module no
+    longer defines would only show there. Every global it (and the functions
+    it calls) loads must resolve in the module or the builtins."""
+    import builtins
+    import dis
+    import types
+
+    seen, todo, missing = set(), [bench.main], []
+    while todo:
+        fn = todo.pop()
+        if fn in seen:
+            continue
+        seen.add(fn)
+        codes = [fn.__code__]
+        while codes:
+            code = codes.pop()
+            codes += [c for c in code.co_consts if isinstance(c, types.CodeType)]
+            for ins in dis.get_instructions(code):
+                if ins.opname != "LOAD_GLOBAL":
+                    continue
+                name = ins.argval
+                obj = getattr(bench, name, getattr(builtins, name, None))
+                if obj is None and not hasattr(bench, name):
+                    missing.append((fn.__name__, name))
+                elif isinstance(obj, types.FunctionType) and obj.__module__ == bench.__name__:
+                    todo.append(obj)
+    assert not missing, missing

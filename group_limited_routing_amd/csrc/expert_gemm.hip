@@ -196,8 +196,11 @@ __device__ __forceinline__ void row_amax_update(uint32_t* hamax, int grow, float
 
 // ---------------------------------------------------------------- stream variant
 // FN = 16-row weight fragments per wave (mode 0: FN/2 gate + FN/2 up),
-// D = depth of the register prefetch ring (in MFMA k-steps).
-template <int MODE, typename AT, bool FP8, bool PACKED, int FN, int D>
+// D = depth of the register prefetch ring (in MFMA k-steps), MR = 16-row
+// blocks of tokens per M-tile (1 or 2): each weight fragment streamed from
+// HBM feeds MR matrix-core steps, so an expert with up to 16 MR rows reads
+// its weights once.
+template <int MODE, typename AT, bool FP8, bool PACKED, int FN, int D, int MR>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
   using WT = typename WTraits<FP8>::W;
   constexpr int KSTEP = WTraits<FP8>::KSTEP;
@@ -205,18 +208,23 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
   constexpr int HALF = FN / 2;
   constexpr int COLS_W = (MODE == 0) ? 16 * HALF : 16 * FN;  // output columns per wave
   constexpr int COLS = 4 * COLS_W;                           // per workgroup
+  static_assert(MR == 1 || MR == 2, "one or two row blocks");
   const int ntn = p.N / COLS;
   const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   TileInfo ti;
-  if (!tile_info(p, mt, kStreamBM, ti)) return;
+  if (!tile_info(p, mt, 16 * MR, ti)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K, N = p.N;
 
-  // Padded rows (r >= rows) repeat the last real row; their results are not stored.
-  const int ar = min(r, ti.rows - 1);
-  const AT* arow = (MODE == 0) ? (const AT*)p.a + (size_t)p.stok[ti.row0 + ar] * K + LANE_K * g
-                               : (const AT*)p.a + (size_t)(ti.row0 + ar) * K + LANE_K * g;
+  // Padded rows (row >= rows) repeat the last real row; their results are not stored.
+  const AT* arow[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const int ar = min(16 * m + r, ti.rows - 1);
+    arow[m] = (MODE == 0) ? (const AT*)p.a + (size_t)p.stok[ti.row0 + ar] * K + LANE_K * g
+                          : (const AT*)p.a + (size_t)(ti.row0 + ar) * K + LANE_K * g;
+  }
   const int ncol0 = nt * COLS + wave * COLS_W;
   const WT* brow[FN];
 #pragma unroll
@@ -237,32 +245,41 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
   }
   constexpr int BSTEP = PACKED ? 16 * KSTEP : KSTEP;  // elements between k-steps of a lane
 
-  f32x4 acc[FN];
+  f32x4 acc[MR][FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int f = 0; f < FN; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nks = K / KSTEP;  // K is a multiple of 128: bf16 nks % 4 == 0, fp8 nks >= 1
   using OR = OpReg<FP8>;
   OR bq[D][FN];
-  OR aq8[FP8 ? D : 1];
+  OR aq8[FP8 ? D : 1][MR];
   using AL16 = typename std::conditional<FP8, ALoad16<uint16_t>, ALoad16<AT>>::type;
-  AL16 aq16[FP8 ? 1 : D];
+  AL16 aq16[FP8 ? 1 : D][MR];
   auto load_step = [&](int d, int s) {
-    if constexpr (FP8)
-      aq8[d] = load_op<true>(arow + (size_t)s * KSTEP);
-    else
-      aq16[d].load((const typename std::conditional<FP8, uint16_t, AT>::type*)arow + (size_t)s * KSTEP);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      if constexpr (FP8)
+        aq8[d][m] = load_op<true>(arow[m] + (size_t)s * KSTEP);
+      else
+        aq16[d][m].load((const typename std::conditional<FP8, uint16_t, AT>::type*)arow[m] +
+                        (size_t)s * KSTEP);
+    }
 #pragma unroll
     for (int f = 0; f < FN; ++f) bq[d][f] = load_w<FP8>(brow[f] + (size_t)s * BSTEP);
   };
   auto consume = [&](int d) {
-    OR a;
-    if constexpr (FP8)
-      a = aq8[d];
-    else
-      a = aq16[d].bits();
 #pragma unroll
-    for (int f = 0; f < FN; ++f) acc[f] = mfma_op(a, bq[d][f], acc[f]);
+    for (int m = 0; m < MR; ++m) {
+      OR a;
+      if constexpr (FP8)
+        a = aq8[d][m];
+      else
+        a = aq16[d][m].bits();
+#pragma unroll
+      for (int f = 0; f < FN; ++f) acc[m][f] = mfma_op(a, bq[d][f], acc[m][f]);
+    }
   };
   // Prologue without branches (a step past the end, possible only when
   // K < D * KSTEP, re-reads the last step and is never consumed).
@@ -291,34 +308,41 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
   for (int d = 0; d < D; ++d)
     if (s0 + D + d < nks) consume(d);
 
+  // Lane (r, g) of row block m holds rows 16 m + 4 g .. + 3 of column r.
   if (MODE == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * g + i;
-      const bool valid = row < ti.rows;
-      float rowmax = 0.f;
+    for (int m = 0; m < MR; ++m) {
 #pragma unroll
-      for (int f = 0; f < HALF; ++f) {
-        const int n = ncol0 + f * 16 + r;
-        if (valid) {
-          const float h = gateup_value<FP8>(p, ti, row, n, acc[f][i], acc[f + HALF][i]);
-          store_h<FP8>(p, (size_t)(ti.row0 + row) * N + n, h);
-          rowmax = fmaxf(rowmax, fabsf(h));
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * m + 4 * g + i;
+        const bool valid = row < ti.rows;
+        float rowmax = 0.f;
+#pragma unroll
+        for (int f = 0; f < HALF; ++f) {
+          const int n = ncol0 + f * 16 + r;
+          if (valid) {
+            const float h = gateup_value<FP8>(p, ti, row, n, acc[m][f][i], acc[m][f + HALF][i]);
+            store_h<FP8>(p, (size_t)(ti.row0 + row) * N + n, h);
+            rowmax = fmaxf(rowmax, fabsf(h));
+          }
         }
+        if constexpr (FP8) row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
       }
-      if constexpr (FP8) row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
     }
   } else {
     uint16_t* out = (uint16_t*)p.out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * g + i;
-      if (row < ti.rows) {
+    for (int m = 0; m < MR; ++m) {
 #pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const int n = ncol0 + f * 16 + r;
-          out[(size_t)(ti.row0 + row) * N + n] =
-              (uint16_t)f32_to_bf16_bits(down_value<FP8>(p, ti, row, n, acc[f][i]));
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * m + 4 * g + i;
+        if (row < ti.rows) {
+#pragma unroll
+          for (int f = 0; f < FN; ++f) {
+            const int n = ncol0 + f * 16 + r;
+            out[(size_t)(ti.row0 + row) * N + n] =
+                (uint16_t)f32_to_bf16_bits(down_value<FP8>(p, ti, row, n, acc[m][f][i]));
+          }
         }
       }
     }
@@ -333,15 +357,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
 // epilogue); each 16x16x128 MFMA takes the weight fragment as its second
 // operand together with the lane's block scale. Same M-tiles, waves and
 // register ring as the streaming bf16/fp8 variant.
-template <int MODE, int FN, int D>
+template <int MODE, int FN, int D, int MR>
 __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
   constexpr int HALF = FN / 2;
   constexpr int COLS_W = (MODE == 0) ? 16 * HALF : 16 * FN;  // output columns per wave
   constexpr int COLS = 4 * COLS_W;                           // per workgroup
+  static_assert(MR == 1 || MR == 2, "one or two row blocks");
   const int ntn = p.N / COLS;
   const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   TileInfo ti;
-  if (!tile_info(p, mt, kStreamBM, ti)) return;
+  if (!tile_info(p, mt, 16 * MR, ti)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K, N = p.N;
@@ -354,9 +379,13 @@ __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
   // a therefore holds step elements 16 a .. + 15 in bytes 0-15 and
   // 64 + 16 a .. + 15 in bytes 16-31: each weight lane (32 consecutive
   // elements, one block scale) then meets exactly its own 32 activations.
-  const int ar = min(r, ti.rows - 1);
-  const uint8_t* arow = (MODE == 0) ? (const uint8_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K + 16 * g
-                                    : (const uint8_t*)p.a + (size_t)(ti.row0 + ar) * K + 16 * g;
+  const uint8_t* arow[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const int ar = min(16 * m + r, ti.rows - 1);
+    arow[m] = (MODE == 0) ? (const uint8_t*)p.a + (size_t)p.stok[ti.row0 + ar] * K + 16 * g
+                          : (const uint8_t*)p.a + (size_t)(ti.row0 + ar) * K + 16 * g;
+  }
   const int ncol0 = nt * COLS + wave * COLS_W;
   const uint8_t* brow[FN];   // this lane's 16 code bytes of step 0
   const uint32_t* srow[FN];  // this lane's scale dword of steps 0..3
@@ -371,17 +400,22 @@ __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
     srow[f] = S + ((size_t)ti.e * (N / 16) + rb) * (K / 512) * 64 + lane;
   }
 
-  f32x4 acc[FN];
+  f32x4 acc[MR][FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int f = 0; f < FN; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nks = K / 128;  // a multiple of 4
-  Op32 aq[D];
+  Op32 aq[D][MR];
   u32x4 bq[D][FN];
   uint32_t sq[D][FN];
   auto load_step = [&](int d, int s) {
-    aq[d].lo = ld16(arow + (size_t)s * 128);
-    aq[d].hi = ld16(arow + (size_t)s * 128 + 64);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      aq[d][m].lo = ld16(arow[m] + (size_t)s * 128);
+      aq[d][m].hi = ld16(arow[m] + (size_t)s * 128 + 64);
+    }
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
       bq[d][f] = ld16_nt(brow[f] + (size_t)s * 1024);
@@ -389,21 +423,24 @@ __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
     }
   };
   auto consume = [&](int d) {
-    i32x8 a;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = (int)aq[d].lo[i];
-      a[4 + i] = (int)aq[d].hi[i];
-    }
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      i32x8 b;
+    for (int m = 0; m < MR; ++m) {
+      i32x8 a;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        b[i] = (int)bq[d][f][i];
-        b[4 + i] = 0;
+        a[i] = (int)aq[d][m].lo[i];
+        a[4 + i] = (int)aq[d][m].hi[i];
       }
-      acc[f] = mfma_fp8_fp4(a, b, (int)(sq[d][f] & 0xffu), acc[f]);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        i32x8 b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b[i] = (int)bq[d][f][i];
+          b[4 + i] = 0;
+        }
+        acc[m][f] = mfma_fp8_fp4(a, b, (int)(sq[d][f] & 0xffu), acc[m][f]);
+      }
     }
   };
 #pragma unroll
@@ -429,33 +466,39 @@ __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
 
   if (MODE == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * g + i;
-      const bool valid = row < ti.rows;
-      const float xs = valid ? p.a_scale[p.stok[ti.row0 + row]] : 0.f;
-      float rowmax = 0.f;
+    for (int m = 0; m < MR; ++m) {
 #pragma unroll
-      for (int f = 0; f < HALF; ++f) {
-        const int n = ncol0 + f * 16 + r;
-        if (valid) {
-          const float h = silu_f32(acc[f][i] * xs) * (acc[f + HALF][i] * xs);
-          ((float*)p.out)[(size_t)(ti.row0 + row) * N + n] = h;
-          rowmax = fmaxf(rowmax, fabsf(h));
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * m + 4 * g + i;
+        const bool valid = row < ti.rows;
+        const float xs = valid ? p.a_scale[p.stok[ti.row0 + row]] : 0.f;
+        float rowmax = 0.f;
+#pragma unroll
+        for (int f = 0; f < HALF; ++f) {
+          const int n = ncol0 + f * 16 + r;
+          if (valid) {
+            const float h = silu_f32(acc[m][f][i] * xs) * (acc[m][f + HALF][i] * xs);
+            ((float*)p.out)[(size_t)(ti.row0 + row) * N + n] = h;
+            rowmax = fmaxf(rowmax, fabsf(h));
+          }
         }
+        row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
       }
-      row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
     }
   } else {
     uint16_t* out = (uint16_t*)p.out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * g + i;
-      if (row < ti.rows) {
-        const float rs = p.a_scale[ti.row0 + row] * p.sw[ti.row0 + row];
+    for (int m = 0; m < MR; ++m) {
 #pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const int n = ncol0 + f * 16 + r;
-          out[(size_t)(ti.row0 + row) * N + n] = (uint16_t)f32_to_bf16_bits(acc[f][i] * rs);
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * m + 4 * g + i;
+        if (row < ti.rows) {
+          const float rs = p.a_scale[ti.row0 + row] * p.sw[ti.row0 + row];
+#pragma unroll
+          for (int f = 0; f < FN; ++f) {
+            const int n = ncol0 + f * 16 + r;
+            out[(size_t)(ti.row0 + row) * N + n] = (uint16_t)f32_to_bf16_bits(acc[m][f][i] * rs);
+          }
         }
       }
     }
@@ -1731,8 +1774,15 @@ int mtile_bound(const Shape& s, int BM) {
 
 bool use_stream_gemm(const Shape& s) {
   // Up to about 16 rows per expert on average the weights are streamed once
-  // per 16-row tile; beyond that the LDS-tiled variant reuses them better.
+  // per M-tile; beyond that the LDS-tiled variant reuses them better.
   return (long long)s.T * s.top_k <= 16LL * s.E;
+}
+
+int stream_bm(const Shape& s) {
+  // Above 8 rows per expert on average a good part of the experts exceed 16
+  // rows (at 16 on average, about 45% of them): 32-row tiles keep such an
+  // expert to one M-tile, so its weights are streamed once.
+  return (long long)s.T * s.top_k > 8LL * s.E ? 2 * kStreamBM : kStreamBM;
 }
 
 // Output columns per workgroup: 4 waves x 16 x FN (down) or x 16 x FN/2
@@ -1745,13 +1795,26 @@ static void launch_stream(const Shape& s, const GemmArgs& g, hipStream_t st) {
   // Few experts running (an expert shard): narrower workgroups, so that
   // about 1024 stream weights at once (one M-tile per expert at decode).
   while (fn > 2 && (long long)s.n_run * (g.N / (fn * per)) < 1024) fn /= 2;
-  dim3 grid(mtile_bound(s, kStreamBM) * (g.N / (fn * per)));
-  if (fn == 8)
-    gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, D><<<grid, 256, 0, st>>>(g);
-  else if (fn == 4)
-    gemm_stream_kernel<MODE, AT, FP8, PACKED, 4, D><<<grid, 256, 0, st>>>(g);
-  else
-    gemm_stream_kernel<MODE, AT, FP8, PACKED, 2, D><<<grid, 256, 0, st>>>(g);
+  const int bm = stream_bm(s);
+  // fp8 operands take twice the registers of bf16: with two row blocks, 8
+  // fragments per wave would leave one wave per SIMD
+  if (FP8 && bm != kStreamBM && fn == 8) fn = 4;
+  dim3 grid(mtile_bound(s, bm) * (g.N / (fn * per)));
+  if (bm == kStreamBM) {
+    if (fn == 8)
+      gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, D, 1><<<grid, 256, 0, st>>>(g);
+    else if (fn == 4)
+      gemm_stream_kernel<MODE, AT, FP8, PACKED, 4, D, 1><<<grid, 256, 0, st>>>(g);
+    else
+      gemm_stream_kernel<MODE, AT, FP8, PACKED, 2, D, 1><<<grid, 256, 0, st>>>(g);
+  } else {
+    if (fn == 8)
+      gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, D, 2><<<grid, 256, 0, st>>>(g);
+    else if (fn == 4)
+      gemm_stream_kernel<MODE, AT, FP8, PACKED, 4, D, 2><<<grid, 256, 0, st>>>(g);
+    else
+      gemm_stream_kernel<MODE, AT, FP8, PACKED, 2, D, 2><<<grid, 256, 0, st>>>(g);
+  }
 }
 
 template <int MODE, typename AT, bool FP8, bool PACKED>
@@ -1776,7 +1839,7 @@ int wide_bm(const Shape& s) {
 }
 
 int forward_list_bm(const Shape& s) {
-  if (use_stream_gemm(s)) return kStreamBM;
+  if (use_stream_gemm(s)) return stream_bm(s);
   if (!s.w_packed) return kTiledBM;
   const int bm = wide_bm(s);
   // packed fp8 weights at 256-row tiles: 512-row tiles for experts beyond 256 rows
@@ -1840,10 +1903,18 @@ static void launch_variant(const Shape& s, const GemmArgs& g, hipStream_t st) {
 template <int MODE>
 static void launch_mx4(const Shape& s, const GemmArgs& g, hipStream_t st) {
   if (use_stream_gemm(s)) {
-    constexpr int FN = 8, D = 2;
-    constexpr int per = (MODE == 0) ? 4 * 16 * FN / 2 : 4 * 16 * FN;
-    dim3 grid(mtile_bound(s, kStreamBM) * (g.N / per));
-    gemm_stream4_kernel<MODE, FN, D><<<grid, 256, 0, st>>>(g);
+    // 8 fragments per wave with one row block, 4 with two (two waves per SIMD)
+    constexpr int D = 2;
+    const int bm = stream_bm(s);
+    if (bm == kStreamBM) {
+      constexpr int FN = 8, per = (MODE == 0) ? 4 * 16 * FN / 2 : 4 * 16 * FN;
+      dim3 grid(mtile_bound(s, bm) * (g.N / per));
+      gemm_stream4_kernel<MODE, FN, D, 1><<<grid, 256, 0, st>>>(g);
+    } else {
+      constexpr int FN = 4, per = (MODE == 0) ? 4 * 16 * FN / 2 : 4 * 16 * FN;
+      dim3 grid(mtile_bound(s, bm) * (g.N / per));
+      gemm_stream4_kernel<MODE, FN, D, 2><<<grid, 256, 0, st>>>(g);
+    }
     return;
   }
   const int BM = wide_bm(s);

@@ -10,7 +10,7 @@
 namespace beam {
 
 // Row tile (tokens per M-tile) of the two expert-GEMM variants.
-constexpr int kStreamBM = 16;   // decode: weight streaming, one MFMA row block
+constexpr int kStreamBM = 16;   // decode: weight streaming, one MFMA row block (or two: stream_bm)
 constexpr int kTiledBM = 128;   // prefill, row-major weights: LDS-staged MFMA tiles
 // M-tile list of the mixed-height DMA GEMMs: 256-row slots, and 512-row tiles
 // (two slots each) for experts with more than 256 rows.
@@ -42,10 +42,13 @@ constexpr int kRouterSplitMaxT = 256;
 
 Layout make_layout(const Shape& s);
 bool use_stream_gemm(const Shape& s);
+// M-tile height of the streaming variants: kStreamBM, or 2 kStreamBM above 8
+// rows per expert on average
+int stream_bm(const Shape& s);
 // prefill with packed weights: M-tile of 128 or 256 rows, from the rows per expert
 int wide_bm(const Shape& s);
 // Row height of the forward's M-tile list (shared by the gate/up and down
-// passes): kStreamBM, kTiledBM, 128, 256, or kMixedBM (256-row slots, 512-row
+// passes): kStreamBM or 2 kStreamBM, kTiledBM, 128, 256, or kMixedBM (256-row slots, 512-row
 // tiles for experts with more than 256 rows).
 int forward_list_bm(const Shape& s);
 int mtile_bound(const Shape& s, int BM);

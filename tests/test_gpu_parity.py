@@ -93,6 +93,28 @@ def test_stream_variant_wide(packed):
     _full_compare("stream wide", cfg, 13, packed)
 
 
+# Between 8 and 16 rows per expert on average the streaming variants take
+# 32-row M-tiles (two row blocks per weight fragment): experts of 17-32 rows
+# in one tile, hot experts over many tiles with a ragged last one.
+@pytest.mark.parametrize("name,T,H,I,x_dtype,w_dtype,bias,packed", [
+    ("bf16 8-fragment waves", 450, 1024, 512, "bf16", "bf16", "normal", False),
+    ("bf16 packed hot", 400, 512, 256, "bf16", "bf16", "hot", True),
+    ("fp32 x", 400, 256, 128, "f32", "bf16", "normal", True),
+    ("fp8 rowmajor", 400, 512, 256, "bf16", "fp8", "normal", False),
+    ("fp8 packed hot", 400, 512, 256, "bf16", "fp8", "hot", True),
+    ("mxfp4", 450, 512, 1024, "bf16", "mxfp4", "normal", True),
+    ("mxfp4 hot", 400, 1024, 512, "bf16", "mxfp4", "hot", True),
+])
+def test_stream_variant_two_row_blocks(name, T, H, I, x_dtype, w_dtype, bias, packed):
+    cfg = _case(T, H, I, x_dtype=x_dtype, w_dtype=w_dtype, bias=bias)
+    assert 8 * 256 < T * 8 <= 16 * 256
+    out, r = _full_compare("stream 32-row " + name, cfg, 31, packed)
+    cnt = r["expert_counts"].cpu().numpy()
+    assert (cnt > 16).sum() >= 4  # experts that a 16-row tile list splits
+    if bias == "hot":
+        assert cnt[:8].min() > 4 * 32  # hot experts span several 32-row tiles
+
+
 @pytest.mark.parametrize("packed", LAYOUTS)
 def test_ragged_tiled_variant(packed):
     cfg = _case(1000, 512, 384)         # 8000 pairs: LDS-tiled GEMMs, ragged tiles

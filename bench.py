@@ -87,12 +87,13 @@ def gateup_kernel(cfg):
     pairs = cfg["T"] * cfg["top_k"]
     xt = "float" if cfg["x_dtype"] == "f32" else "unsigned short"
     fp8 = cfg["w_dtype"] == "fp8"
+    E = cfg["n_experts"]
     if cfg["w_dtype"] == "mxfp4":
-        if pairs <= 16 * cfg["n_experts"]:
-            return "gemm_stream4_kernel<0, 8, 2>"
-        return f"gemm_dma4_kernel<0, {256 if pairs >= 96 * cfg['n_experts'] else 128}>"
-    if pairs <= 16 * cfg["n_experts"]:
-        return f"gemm_stream_kernel<0, {'unsigned char' if fp8 else xt}, {str(fp8).lower()}, true, ...>"
+        if pairs <= 12 * E:  # streamed: 16-row tiles up to 8 rows per expert, else 32
+            return "gemm_stream4_kernel<0, 8, 2, 1>" if pairs <= 8 * E else "gemm_stream4_kernel<0, 4, 2, 2>"
+        return f"gemm_dma4_kernel<0, {256 if pairs >= 96 * E else 128}>"
+    if not fp8 and pairs <= 16 * E:  # packed fp8 weights always take the DMA variant
+        return f"gemm_stream_kernel<0, {xt}, false, true, ...>"
     dma = fp8 or xt == "unsigned short"
     bm = 256 if pairs >= (96 if dma else 192) * cfg["n_experts"] else 128
     if cfg["hidden"] % 256:

@@ -156,6 +156,24 @@ def test_counter_summaries_match_the_mixed_fp8_kernel(sandbox):
     assert bench.gateup_kernel(workloads.workload("fp8")) == "gemm_dma8_mixed_kernel<0>"
 
 
+def test_gateup_kernel_follows_the_launcher_rules():
+    """The kernel named for the roofline is the one the library picks: bf16
+    weights stream up to 16 rows per expert on average, MXFP4 up to 12 (32-row
+    tiles above 8), packed fp8 never."""
+    import bench
+    import workloads
+    d = workloads.workload("decode")
+    assert bench.gateup_kernel(d).startswith("gemm_stream_kernel<0, unsigned short, false, true")
+    assert bench.gateup_kernel(dict(d, T=600)) == "gemm_dma_kernel<0, 128>"
+    assert bench.gateup_kernel(workloads.workload("prefill")) == "gemm_dma_kernel<0, 256>"
+    m = workloads.workload("mxfp4")
+    assert bench.gateup_kernel(m) == "gemm_stream4_kernel<0, 8, 2, 1>"
+    assert bench.gateup_kernel(dict(m, T=350)) == "gemm_stream4_kernel<0, 4, 2, 2>"
+    assert bench.gateup_kernel(dict(m, T=400)) == "gemm_dma4_kernel<0, 128>"
+    f = workloads.workload("fp8")
+    assert bench.gateup_kernel(dict(f, T=64)) == "gemm_dma8_kernel<0, 128>"
+
+
 def test_every_global_name_main_uses_exists():
     """bench.main() only runs on a GPU machine; a name it calls that the module no
     longer defines would only show there. Every global it (and the functions

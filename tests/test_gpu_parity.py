@@ -101,13 +101,13 @@ def test_stream_variant_wide(packed):
     ("bf16 packed hot", 400, 512, 256, "bf16", "bf16", "hot", True),
     ("fp32 x", 400, 256, 128, "f32", "bf16", "normal", True),
     ("fp8 rowmajor", 400, 512, 256, "bf16", "fp8", "normal", False),
-    ("fp8 packed hot", 400, 512, 256, "bf16", "fp8", "hot", True),
-    ("mxfp4", 450, 512, 1024, "bf16", "mxfp4", "normal", True),
-    ("mxfp4 hot", 400, 1024, 512, "bf16", "mxfp4", "hot", True),
+    ("fp8 rowmajor hot", 400, 512, 256, "bf16", "fp8", "hot", False),
+    ("mxfp4", 350, 512, 1024, "bf16", "mxfp4", "normal", True),
+    ("mxfp4 hot", 370, 1024, 512, "bf16", "mxfp4", "hot", True),
 ])
 def test_stream_variant_two_row_blocks(name, T, H, I, x_dtype, w_dtype, bias, packed):
     cfg = _case(T, H, I, x_dtype=x_dtype, w_dtype=w_dtype, bias=bias)
-    assert 8 * 256 < T * 8 <= 16 * 256
+    assert 8 * 256 < T * 8 <= (12 if w_dtype == "mxfp4" else 16) * 256
     out, r = _full_compare("stream 32-row " + name, cfg, 31, packed)
     cnt = r["expert_counts"].cpu().numpy()
     assert (cnt > 16).sum() >= 4  # experts that a 16-row tile list splits
@@ -134,8 +134,17 @@ def test_wide_variant_256_rows():
 
 @pytest.mark.parametrize("packed", LAYOUTS)
 def test_fp8_stream_variant(packed):
+    # row-major fp8 weights stream; packed ones take the DMA variant at any batch
     cfg = _case(200, 512, 256, w_dtype="fp8")
     _full_compare("fp8 stream", cfg, 6, packed)
+
+
+@pytest.mark.parametrize("T", [1, 64, 500])
+def test_fp8_packed_decode_batches_take_the_dma_variant(T):
+    """Packed fp8 weights never stream: one to a few rows per expert in
+    128-row DMA tiles (most of each tile's rows absent)."""
+    cfg = _case(T, 512, 256, w_dtype="fp8")
+    _full_compare(f"fp8 packed T={T}", cfg, 37, True)
 
 
 @pytest.mark.parametrize("packed", LAYOUTS)

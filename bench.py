@@ -124,9 +124,9 @@ def describe(cfg):
 
 
 # Bytes per element of the intermediate h as the gate/up launch stores it
-# for the down launch (bf16 weights: bf16 h; quantised weights: fp32 h, then
-# one E4M3 code per element).
-H_STORE_BYTES = {"bf16": 2, "fp8": 4, "mxfp4": 4}
+# (bf16 with every weight type; quantised weights add one E4M3 code per
+# element, counted as h_codes).
+H_STORE_BYTES = 2
 
 
 def quantised(cfg):
@@ -161,8 +161,7 @@ def design_overhead(cfg):
     quantised weights also the E4M3 codes of x and of h (written, read)."""
     T, H, I, k = cfg["T"], cfg["hidden"], cfg["intermediate"], cfg["top_k"]
     P = T * k
-    hb = H_STORE_BYTES[cfg["w_dtype"]]
-    out = {"h_round_trip": 2 * P * I * hb, "y_round_trip": 2 * P * H * 2}
+    out = {"h_round_trip": 2 * P * I * H_STORE_BYTES, "y_round_trip": 2 * P * H * 2}
     if quantised(cfg):
         out["x_codes"] = 2 * T * H
         out["h_codes"] = 2 * P * I

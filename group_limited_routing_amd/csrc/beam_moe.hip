@@ -54,7 +54,7 @@ Layout make_layout(const Shape& s) {
     L.xq = take(T * H);      // e4m3 codes of x, per-token scale
     L.xs = take(T * 4);
     L.hamax = take(P * 4);   // running max |h| per sorted row (float bits)
-    L.h = take(P * I * 4);   // fp32 SwiGLU output before quantisation
+    L.h = take(P * I * 2);   // bf16 SwiGLU output before quantisation
     L.hq = take(P * I);      // its e4m3 codes
     L.hs = take(P * 4);      // per-row scale of the quantised h
   } else {
@@ -489,7 +489,7 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
     uint8_t* xq = ws + L.xq;
     float* xs = (float*)(ws + L.xs);
     uint32_t* hamax = (uint32_t*)(ws + L.hamax);
-    float* hf = (float*)(ws + L.h);
+    uint16_t* hb = (uint16_t*)(ws + L.h);
     float* hs = (float*)(ws + L.hs);
     uint8_t* hq = ws + L.hq;
     STAGE(BEAM_STAGE_QUANT_X, launch_quant_x(x, s.x_f32, T, s.H, k, xq, xs, hamax, st));
@@ -499,12 +499,12 @@ beam_status forward_impl(const beam_moe_config* cfg, int32_t T, const void* x,
     g.w1 = w_up;
     g.ws0 = (const float*)w_gate_scale;
     g.ws1 = (const float*)w_up_scale;
-    g.out = hf;
+    g.out = hb;
     g.hamax = hamax;
     g.K = s.H;
     g.N = s.I;
     STAGE(BEAM_STAGE_GATEUP, launch_gateup(s, g, st));
-    STAGE(BEAM_STAGE_QUANT_H, launch_quant_h(hf, hamax, T * k, s.I, hq, hs, st));
+    STAGE(BEAM_STAGE_QUANT_H, launch_quant_h(hb, hamax, T * k, s.I, hq, hs, st));
     g.a = hq;
     g.a_scale = hs;
     g.w0 = w_down;

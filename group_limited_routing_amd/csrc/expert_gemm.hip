@@ -26,8 +26,9 @@
 // Weights are bf16 (16x16x32 bf16 MFMA) or OCP E4M3 codes with one fp32
 // scale per output row (16x16x128 fp8 MFMA). With fp8 weights the A operand
 // is E4M3 too (x quantised per token, h per row); the scales are applied to
-// the fp32 accumulators in the epilogue, and the gate/up pass writes fp32 h
-// and records each row's max |h| for the quantisation of the down pass.
+// the fp32 accumulators in the epilogue, and the gate/up pass writes h as
+// bf16 (as with bf16 weights) and records each row's max |h| of the stored
+// values for the per-row quantisation of the down pass's input.
 #include "common.h"
 #include "internal.h"
 
@@ -176,12 +177,12 @@ __device__ __forceinline__ float down_value(const GemmArgs& p, const TileInfo& t
   }
 }
 
-template <bool FP8>
-__device__ __forceinline__ void store_h(const GemmArgs& p, size_t off, float h) {
-  if constexpr (FP8)
-    ((float*)p.out)[off] = h;
-  else
-    ((uint16_t*)p.out)[off] = (uint16_t)f32_to_bf16_bits(h);
+// h is stored as bf16 (round to nearest even); returns the stored value,
+// whose magnitude enters the row's max |h| on the quantised paths.
+__device__ __forceinline__ float store_h(const GemmArgs& p, size_t off, float h) {
+  const uint32_t b = f32_to_bf16_bits(h);
+  ((uint16_t*)p.out)[off] = (uint16_t)b;
+  return bf16_bits_to_f32(b);
 }
 
 // Row-wise max |h| over the 16 columns a lane group holds, then one atomicMax
@@ -322,8 +323,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs p) {
           const int n = ncol0 + f * 16 + r;
           if (valid) {
             const float h = gateup_value<FP8>(p, ti, row, n, acc[m][f][i], acc[m][f + HALF][i]);
-            store_h<FP8>(p, (size_t)(ti.row0 + row) * N + n, h);
-            rowmax = fmaxf(rowmax, fabsf(h));
+            const float hs = store_h(p, (size_t)(ti.row0 + row) * N + n, h);
+            rowmax = fmaxf(rowmax, fabsf(hs));
           }
         }
         if constexpr (FP8) row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
@@ -478,8 +479,8 @@ __global__ __launch_bounds__(256) void gemm_stream4_kernel(GemmArgs p) {
           const int n = ncol0 + f * 16 + r;
           if (valid) {
             const float h = silu_f32(acc[m][f][i] * xs) * (acc[m][f + HALF][i] * xs);
-            ((float*)p.out)[(size_t)(ti.row0 + row) * N + n] = h;
-            rowmax = fmaxf(rowmax, fabsf(h));
+            const float hs = store_h(p, (size_t)(ti.row0 + row) * N + n, h);
+            rowmax = fmaxf(rowmax, fabsf(hs));
           }
         }
         row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
@@ -664,8 +665,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(GemmArgs p) {
           const int n = n0 + wn * 32 + fn * 16 + r;
           if (valid) {
             const float h = gateup_value<FP8>(p, ti, row, n, acc[fm][fn][i], acc[fm][fn + 2][i]);
-            store_h<FP8>(p, (size_t)(ti.row0 + row) * N + n, h);
-            rowmax = fmaxf(rowmax, fabsf(h));
+            const float hs = store_h(p, (size_t)(ti.row0 + row) * N + n, h);
+            rowmax = fmaxf(rowmax, fabsf(hs));
           }
         }
         if constexpr (FP8) row_amax_update(p.hamax, ti.row0 + row, rowmax, valid);
@@ -733,16 +734,17 @@ __device__ __forceinline__ void transposed_epilogue(const GemmArgs& p, const Til
             uv = uv * xs * cs1[fn][i];
           }
           h[i] = valid ? silu_f32(gv) * uv : 0.f;
-          rowmax = fmaxf(rowmax, fabsf(h[i]));
         }
-        if (valid) {
-          if constexpr (FP8)
-            st16((float*)p.out + orow + n, u32x4{__float_as_uint(h[0]), __float_as_uint(h[1]),
-                                                 __float_as_uint(h[2]), __float_as_uint(h[3])});
-          else
-            *reinterpret_cast<u32x2*>((uint16_t*)p.out + orow + n) =
-                u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+        // h is stored as bf16 (round to nearest even); the quantised paths
+        // take the row's max |h| over the stored values
+        const u32x2 hb = u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+        if constexpr (FP8) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            rowmax = fmaxf(rowmax, fmaxf(fabsf(bf16_bits_to_f32(hb[i] & 0xffffu)),
+                                         fabsf(bf16_bits_to_f32(hb[i] >> 16))));
         }
+        if (valid) *reinterpret_cast<u32x2*>((uint16_t*)p.out + orow + n) = hb;
       }
       if constexpr (FP8) {
         // the row's 32 columns of this wave sit in lanes r, r + 16, r + 32, r + 48
@@ -2244,19 +2246,22 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const XT* __restrict__ x, 
 }
 
 // One workgroup per sorted row of h.
-__global__ __launch_bounds__(256) void quant_h_kernel(const float* __restrict__ hf,
+__global__ __launch_bounds__(256) void quant_h_kernel(const uint16_t* __restrict__ hb,
                                                       const uint32_t* __restrict__ hamax, int I,
                                                       uint8_t* __restrict__ hq,
                                                       float* __restrict__ hs) {
   const size_t row = blockIdx.x;
   const float amax = __uint_as_float(hamax[row]);
   const float inv = amax > 0.f ? 448.0f / amax : 0.f;
-  for (int c = threadIdx.x * 4; c < I; c += 256 * 4) {
-    const u32x4 v = ld16_nt(hf + row * I + c);  // h is read once
-    uint32_t w = 0u;
+  for (int c = threadIdx.x * 8; c < I; c += 256 * 8) {
+    const u32x4 v = ld16_nt(hb + row * I + c);  // h is read once
+    uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w |= f32_to_e4m3(__uint_as_float(v[i]) * inv) << (8 * i);
-    *reinterpret_cast<uint32_t*>(hq + row * I + c) = w;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t bits = (v[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      w[i >> 2] |= f32_to_e4m3(bf16_bits_to_f32(bits) * inv) << (8 * (i & 3));
+    }
+    *reinterpret_cast<u32x2*>(hq + row * I + c) = u32x2{w[0], w[1]};
   }
   if (threadIdx.x == 0) hs[row] = amax > 0.f ? amax / 448.0f : 1.0f;
 }
@@ -2270,9 +2275,9 @@ hipError_t launch_quant_x(const void* x, int x_f32, int T, int H, int k, uint8_t
   return hipGetLastError();
 }
 
-hipError_t launch_quant_h(const float* hf, const uint32_t* hamax, int rows, int I, uint8_t* hq,
+hipError_t launch_quant_h(const uint16_t* hb, const uint32_t* hamax, int rows, int I, uint8_t* hq,
                           float* hs, hipStream_t st) {
-  quant_h_kernel<<<rows, 256, 0, st>>>(hf, hamax, I, hq, hs);
+  quant_h_kernel<<<rows, 256, 0, st>>>(hb, hamax, I, hq, hs);
   return hipGetLastError();
 }
 

@@ -159,7 +159,7 @@ hipError_t launch_pack_t(const void* src, void* dst, int E, int rows, int cols, 
 hipError_t launch_bias_step(float* bias, const int32_t* counts, float gamma, hipStream_t st);
 hipError_t launch_quant_x(const void* x, int x_f32, int T, int H, int k, uint8_t* xq, float* xs,
                           uint32_t* hamax, hipStream_t st);
-hipError_t launch_quant_h(const float* hf, const uint32_t* hamax, int rows, int I, uint8_t* hq,
+hipError_t launch_quant_h(const uint16_t* hb, const uint32_t* hamax, int rows, int I, uint8_t* hq,
                           float* hs, hipStream_t st);
 
 }  // namespace beam

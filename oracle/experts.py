@@ -23,7 +23,7 @@ stream one expert at a time at the full 20 GB layer size.
 import numpy as np
 
 from .routing import route, weights_for
-from . import e4m3
+from . import bf16, e4m3
 
 
 def silu(v):
@@ -40,15 +40,16 @@ def silu(v):
 def expert_ffn(x_rows, w_gate_e, w_up_e, w_down_e, quantize_h=False):
     """One SwiGLU expert on a block of rows: [n, H] -> [n, H] (float64).
 
-    ``quantize_h`` passes the [n, I] intermediate through per-row E4M3
-    quantise/dequantise before the down projection (fp8 experts only).
+    ``quantize_h`` (fp8 and MXFP4 experts only) takes the [n, I]
+    intermediate as it is stored, bf16 (``bf16.round_to_bf16``), through
+    per-row E4M3 quantise/dequantise before the down projection.
     """
     xr = np.asarray(x_rows, dtype=np.float64)
     g = xr @ np.asarray(w_gate_e, dtype=np.float64).T
     u = xr @ np.asarray(w_up_e, dtype=np.float64).T
     h = silu(g) * u
     if quantize_h:
-        h = e4m3.fake_quantize_rows(h)
+        h = e4m3.fake_quantize_rows(bf16.round_to_bf16(h))
     return h @ np.asarray(w_down_e, dtype=np.float64).T
 
 

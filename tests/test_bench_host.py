@@ -67,6 +67,7 @@ def test_design_overhead_counts_the_round_trips():
     # quantised weights add the E4M3 codes of x and h
     f = bench.design_overhead(workloads.workload("fp8"))
     assert f["x_codes"] == 2 * 8192 * H and f["h_codes"] == 2 * 8192 * 8 * I
+    assert f["h_round_trip"] == 2 * 8192 * 8 * I * 2  # h is stored as bf16 there too
 
 
 def _write_counters(path, rows):

@@ -161,3 +161,12 @@ def test_row_quantiser_dividing_by_the_scale_is_caught(monkeypatch):
         return codes, np.where(zero, np.float32(1.0), scale).astype(np.float32)
     monkeypatch.setattr(e4m3, "quantize_rows", quantize_rows_div)
     assert _fails(te.test_quantize_rows_multiplies_by_the_fp32_reciprocal)
+
+
+def test_quantised_h_without_bf16_storage_is_caught(monkeypatch):
+    """Quantising the fp32 intermediate directly instead of its stored bf16
+    values."""
+    import oracle.bf16 as ob16
+    import test_oracle_bf16 as tb16
+    monkeypatch.setattr(ob16, "round_to_bf16", lambda v: np.asarray(v, dtype=np.float64))
+    assert _fails(tb16.test_quantised_expert_quantises_the_stored_bf16_h)

@@ -47,7 +47,8 @@ workload; --calibrate-copy runs one plain device copy of 1 GiB before the
 timed region (for counter calibration); --summarize DIR prints a summary of
 a rocprofv3 output directory (kernel stats or counter collection);
 --traffic FETCH_DIR WRITE_DIR --workload W writes the counter summary that
-the traffic field reads.
+the traffic field reads (W = ep_shard: the expert-shard line's launches in
+a decode run).
 """
 
 import argparse
@@ -446,7 +447,8 @@ def ep_shard_line(dev, bench, gpus=8, steps=50):
                         f"({gpus} x 64) routed over all experts, this shard's {pairs} pairs "
                         f"on {active} active experts, bf16 weights (its {e1} experts only)",
             "ms_per_step": round(ms, 4), "steps": steps,
-            "roofline": dict(roofline(gb, 4.0 * pairs * H * I, gu_ms / 1e3, "bf16"),
+            "roofline": dict(roofline(gb, 4.0 * pairs * H * I, gu_ms / 1e3, "bf16",
+                                      traffic=stored_figure("ep_shard")),
                              kernel="gate/up", launch_ms=round(gu_ms, 4), algorithmic_bytes=gb)}
 
 
@@ -668,6 +670,16 @@ def write_traffic(fetch_dir, write_dir, workload):
     region (the largest copyBuffer dispatch of the run)."""
     import re
     pats = {"gateup": re.compile(r"beam::gemm_\w+<0[,>]"), "down": re.compile(r"beam::gemm_\w+<1[,>]")}
+    run = (f"--workload {workload} --steps 3 --warmup 1 --no-prefill --no-residual --no-backward "
+           "--no-shard --no-fp8 --no-cpu-baseline --calibrate-copy")
+    if workload == "ep_shard":
+        # the decode run with its expert-shard line: the shard's 512 tokens
+        # (about 15 rows per expert) take the 32-row streaming kernels, the
+        # 64 decode tokens the 16-row ones
+        pats = {"gateup": re.compile(r"beam::gemm_stream_kernel<0, .*, 2>\("),
+                "down": re.compile(r"beam::gemm_stream_kernel<1, .*, 2>\(")}
+        run = ("--workload decode --steps 3 --warmup 1 --no-prefill --no-residual --no-backward "
+               "--no-fp8 --no-cpu-baseline --calibrate-copy")
     out = {}
     for name, d in (("fetch", fetch_dir), ("write", write_dir)):
         rows = _counter_rows(d)
@@ -683,9 +695,7 @@ def write_traffic(fetch_dir, write_dir, workload):
     f, w = out["fetch"], out["write"]
     hbm = {st: (f[st]["kib"] * f["factor"] + w[st]["kib"] * w["factor"]) * 1024 for st in pats}
     cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --kernel-include-regex 'gemm|copyBuffer' "
-           "-d <dir> -o run --output-format csv "
-           f"-- python3 /root/repo/bench.py --workload {workload} --steps 3 --warmup 1 --no-prefill "
-           "--no-residual --no-backward --no-shard --no-fp8 --no-cpu-baseline --calibrate-copy")
+           f"-d <dir> -o run --output-format csv -- python3 /root/repo/bench.py {run}")
     path = os.path.join(ROOT, "profiles", f"gateup_{workload}_counters.txt")
     with open(path, "w") as fh:
         fh.write(f"# HBM traffic of the gate/up and down grouped GEMMs, workload {workload}, one MI355X\n")
@@ -755,7 +765,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "prefill", "skewed", "fp8", "mxfp4", "mxfp4_prefill"])
+                    choices=["tiny", "decode", "prefill", "skewed", "fp8", "mxfp4", "mxfp4_prefill",
+                             "ep_shard"])
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill and skewed lines (decode runs)")
@@ -784,6 +795,9 @@ def main():
     if args.traffic:
         write_traffic(args.traffic[0], args.traffic[1], args.workload)
         return 0
+    if args.workload == "ep_shard":
+        raise SystemExit("--workload ep_shard only names the counter summary of --traffic; the "
+                         "expert-shard line runs with the decode workload")
     if args.wgrad_traffic:
         write_wgrad_traffic(args.wgrad_traffic[0], args.wgrad_traffic[1])
         return 0

@@ -175,6 +175,26 @@ def test_gateup_kernel_follows_the_launcher_rules():
     assert bench.gateup_kernel(dict(f, T=64)) == "gemm_dma8_kernel<0, 128>"
 
 
+def test_shard_traffic_takes_the_32_row_stream_launches(sandbox):
+    """In the decode run that carries the expert-shard line, the shard's
+    launches are the 32-row streaming kernels and the decode ones the 16-row
+    kernels: the ep_shard summary must take only the former."""
+    dec_g = "void beam::gemm_stream_kernel<0, unsigned short, false, true, 8, 2, 1>(beam::GemmArgs)"
+    dec_d = "void beam::gemm_stream_kernel<1, unsigned short, false, true, 8, 2, 1>(beam::GemmArgs)"
+    sh_g = "void beam::gemm_stream_kernel<0, unsigned short, false, true, 2, 2, 2>(beam::GemmArgs)"
+    sh_d = "void beam::gemm_stream_kernel<1, unsigned short, false, true, 2, 2, 2>(beam::GemmArgs)"
+    for d, c in (("f", "FETCH_SIZE"), ("w", "WRITE_SIZE")):
+        _write_counters(sandbox / d, [(1, COPY, c, 524288 if c == "FETCH_SIZE" else 1048576, 0, 1),
+                                      (2, dec_g, c, 9000, 0, 1), (3, dec_d, c, 8000, 0, 1),
+                                      (4, sh_g, c, 700, 0, 1), (5, sh_d, c, 300, 0, 1),
+                                      (6, sh_g, c, 900, 0, 1)])
+    bench.write_traffic(str(sandbox / "f"), str(sandbox / "w"), "ep_shard")
+    assert bench.stored_figure("ep_shard") == (800 * 2 + 800) * 1024
+    assert bench.stored_figure("ep_shard", key="down_hbm_bytes_per_launch") == (300 * 2 + 300) * 1024
+    text = open(os.path.join(bench.ROOT, "profiles", "gateup_ep_shard_counters.txt")).read()
+    assert "--workload decode" in text and "--no-shard" not in text
+
+
 def test_every_global_name_main_uses_exists():
     """bench.main() only runs on a GPU machine; a name it calls that the module no
     longer defines would only show there. Every global it (and the functions

@@ -1792,11 +1792,24 @@ int stream_bm(const Shape& s) {
   return (long long)s.T * s.top_k > 8LL * s.E ? 2 * kStreamBM : kStreamBM;
 }
 
+// Register-ring depth (k-steps in flight per wave) of the streaming kernels
+// for FN fragments per wave and MR row blocks.
+constexpr int stream_depth(int fn, int mr) { return (fn == 2) ? 4 : 2; }
+
+template <int MODE, typename AT, bool FP8, bool PACKED, int MR>
+static void launch_stream_mr(dim3 grid, int fn, const GemmArgs& g, hipStream_t st) {
+  if (fn == 8)
+    gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, stream_depth(8, MR), MR><<<grid, 256, 0, st>>>(g);
+  else if (fn == 4)
+    gemm_stream_kernel<MODE, AT, FP8, PACKED, 4, stream_depth(4, MR), MR><<<grid, 256, 0, st>>>(g);
+  else
+    gemm_stream_kernel<MODE, AT, FP8, PACKED, 2, stream_depth(2, MR), MR><<<grid, 256, 0, st>>>(g);
+}
+
 // Output columns per workgroup: 4 waves x 16 x FN (down) or x 16 x FN/2
 // (gate/up). FN = 8 where it divides N, else 4, else 2 (N is a multiple of 128).
 template <int MODE, typename AT, bool FP8, bool PACKED>
 static void launch_stream(const Shape& s, const GemmArgs& g, hipStream_t st) {
-  constexpr int D = 2;
   const int per = (MODE == 0) ? 32 : 64;  // columns per workgroup per unit of FN
   int fn = (g.N % (8 * per) == 0) ? 8 : (g.N % (4 * per) == 0) ? 4 : 2;
   // Few experts running (an expert shard): narrower workgroups, so that
@@ -1807,21 +1820,10 @@ static void launch_stream(const Shape& s, const GemmArgs& g, hipStream_t st) {
   // fragments per wave would leave one wave per SIMD
   if (FP8 && bm != kStreamBM && fn == 8) fn = 4;
   dim3 grid(mtile_bound(s, bm) * (g.N / (fn * per)));
-  if (bm == kStreamBM) {
-    if (fn == 8)
-      gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, D, 1><<<grid, 256, 0, st>>>(g);
-    else if (fn == 4)
-      gemm_stream_kernel<MODE, AT, FP8, PACKED, 4, D, 1><<<grid, 256, 0, st>>>(g);
-    else
-      gemm_stream_kernel<MODE, AT, FP8, PACKED, 2, D, 1><<<grid, 256, 0, st>>>(g);
-  } else {
-    if (fn == 8)
-      gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, D, 2><<<grid, 256, 0, st>>>(g);
-    else if (fn == 4)
-      gemm_stream_kernel<MODE, AT, FP8, PACKED, 4, D, 2><<<grid, 256, 0, st>>>(g);
-    else
-      gemm_stream_kernel<MODE, AT, FP8, PACKED, 2, D, 2><<<grid, 256, 0, st>>>(g);
-  }
+  if (bm == kStreamBM)
+    launch_stream_mr<MODE, AT, FP8, PACKED, 1>(grid, fn, g, st);
+  else
+    launch_stream_mr<MODE, AT, FP8, PACKED, 2>(grid, fn, g, st);
 }
 
 template <int MODE, typename AT, bool FP8, bool PACKED>
@@ -1911,7 +1913,7 @@ template <int MODE>
 static void launch_mx4(const Shape& s, const GemmArgs& g, hipStream_t st) {
   if (use_stream_gemm(s)) {
     // 8 fragments per wave with one row block, 4 with two (two waves per SIMD)
-    constexpr int D = 2;
+    constexpr int D = 2;  // register-ring depth
     const int bm = stream_bm(s);
     if (bm == kStreamBM) {
       constexpr int FN = 8, per = (MODE == 0) ? 4 * 16 * FN / 2 : 4 * 16 * FN;

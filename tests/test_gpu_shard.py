@@ -112,6 +112,13 @@ def test_shards_bf16_eight_way():
     _run("bf16 8 shards", _case(300, 512, 256), 41, list(range(0, 257, 32)), packed=False)
 
 
+def test_shards_bf16_packed_decode_batch():
+    """Eight shards of 32 experts at a decode-sized batch (about 6 rows per
+    expert): 16-row streaming tiles with 2 fragments per wave and the deeper
+    register ring that narrow waves take."""
+    _run("bf16 packed decode batch", _case(200, 1024, 512), 45, list(range(0, 257, 32)), packed=True)
+
+
 def test_shards_bf16_packed_uneven():
     _run("bf16 packed uneven", _case(1000, 512, 256), 42, [0, 1, 100, 255, 256], packed=True)
 

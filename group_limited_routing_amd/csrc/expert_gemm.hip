@@ -1793,17 +1793,24 @@ int stream_bm(const Shape& s) {
 }
 
 // Register-ring depth (k-steps in flight per wave) of the streaming kernels
-// for FN fragments per wave and MR row blocks.
-constexpr int stream_depth(int fn, int mr) { return (fn == 2) ? 4 : 2; }
+// for FN fragments per wave and MR row blocks: 4 for waves of 2 fragments (the
+// narrow workgroups of an expert shard, which would otherwise keep 4 KB in
+// flight) and for the bf16 decode waves (8 fragments, one row block, bf16
+// tokens: still two waves per SIMD); else 2, which keeps wider operands (fp8,
+// fp32 tokens) and two row blocks at two waves per SIMD.
+constexpr int stream_depth(int fn, int mr, bool bf16_ops) {
+  return (fn == 2 || (fn == 8 && mr == 1 && bf16_ops)) ? 4 : 2;
+}
 
 template <int MODE, typename AT, bool FP8, bool PACKED, int MR>
 static void launch_stream_mr(dim3 grid, int fn, const GemmArgs& g, hipStream_t st) {
+  constexpr bool B16 = !FP8 && std::is_same<AT, uint16_t>::value;
   if (fn == 8)
-    gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, stream_depth(8, MR), MR><<<grid, 256, 0, st>>>(g);
+    gemm_stream_kernel<MODE, AT, FP8, PACKED, 8, stream_depth(8, MR, B16), MR><<<grid, 256, 0, st>>>(g);
   else if (fn == 4)
-    gemm_stream_kernel<MODE, AT, FP8, PACKED, 4, stream_depth(4, MR), MR><<<grid, 256, 0, st>>>(g);
+    gemm_stream_kernel<MODE, AT, FP8, PACKED, 4, stream_depth(4, MR, B16), MR><<<grid, 256, 0, st>>>(g);
   else
-    gemm_stream_kernel<MODE, AT, FP8, PACKED, 2, stream_depth(2, MR), MR><<<grid, 256, 0, st>>>(g);
+    gemm_stream_kernel<MODE, AT, FP8, PACKED, 2, stream_depth(2, MR, B16), MR><<<grid, 256, 0, st>>>(g);
 }
 
 // Output columns per workgroup: 4 waves x 16 x FN (down) or x 16 x FN/2
@@ -1912,17 +1919,17 @@ static void launch_variant(const Shape& s, const GemmArgs& g, hipStream_t st) {
 template <int MODE>
 static void launch_mx4(const Shape& s, const GemmArgs& g, hipStream_t st) {
   if (use_stream_gemm(s)) {
-    // 8 fragments per wave with one row block, 4 with two (two waves per SIMD)
-    constexpr int D = 2;  // register-ring depth
+    // 8 fragments per wave with one row block (register ring 4 k-steps deep),
+    // 4 with two (ring depth 2, two waves per SIMD)
     const int bm = stream_bm(s);
     if (bm == kStreamBM) {
       constexpr int FN = 8, per = (MODE == 0) ? 4 * 16 * FN / 2 : 4 * 16 * FN;
       dim3 grid(mtile_bound(s, bm) * (g.N / per));
-      gemm_stream4_kernel<MODE, FN, D, 1><<<grid, 256, 0, st>>>(g);
+      gemm_stream4_kernel<MODE, FN, 4, 1><<<grid, 256, 0, st>>>(g);
     } else {
       constexpr int FN = 4, per = (MODE == 0) ? 4 * 16 * FN / 2 : 4 * 16 * FN;
       dim3 grid(mtile_bound(s, bm) * (g.N / per));
-      gemm_stream4_kernel<MODE, FN, D, 2><<<grid, 256, 0, st>>>(g);
+      gemm_stream4_kernel<MODE, FN, 2, 2><<<grid, 256, 0, st>>>(g);
     }
     return;
   }

@@ -91,7 +91,7 @@ def gateup_kernel(cfg):
     E = cfg["n_experts"]
     if cfg["w_dtype"] == "mxfp4":
         if pairs <= 12 * E:  # streamed: 16-row tiles up to 8 rows per expert, else 32
-            return "gemm_stream4_kernel<0, 8, 2, 1>" if pairs <= 8 * E else "gemm_stream4_kernel<0, 4, 2, 2>"
+            return "gemm_stream4_kernel<0, 8, 4, 1>" if pairs <= 8 * E else "gemm_stream4_kernel<0, 4, 2, 2>"
         return f"gemm_dma4_kernel<0, {256 if pairs >= 96 * E else 128}>"
     if not fp8 and pairs <= 16 * E:  # packed fp8 weights always take the DMA variant
         return f"gemm_stream_kernel<0, {xt}, false, true, ...>"

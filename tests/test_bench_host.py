@@ -168,7 +168,7 @@ def test_gateup_kernel_follows_the_launcher_rules():
     assert bench.gateup_kernel(dict(d, T=600)) == "gemm_dma_kernel<0, 128>"
     assert bench.gateup_kernel(workloads.workload("prefill")) == "gemm_dma_kernel<0, 256>"
     m = workloads.workload("mxfp4")
-    assert bench.gateup_kernel(m) == "gemm_stream4_kernel<0, 8, 2, 1>"
+    assert bench.gateup_kernel(m) == "gemm_stream4_kernel<0, 8, 4, 1>"
     assert bench.gateup_kernel(dict(m, T=350)) == "gemm_stream4_kernel<0, 4, 2, 2>"
     assert bench.gateup_kernel(dict(m, T=400)) == "gemm_dma4_kernel<0, 128>"
     f = workloads.workload("fp8")

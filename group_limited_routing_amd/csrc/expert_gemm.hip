@@ -1795,11 +1795,11 @@ int stream_bm(const Shape& s) {
 // Register-ring depth (k-steps in flight per wave) of the streaming kernels
 // for FN fragments per wave and MR row blocks: 4 for waves of 2 fragments (the
 // narrow workgroups of an expert shard, which would otherwise keep 4 KB in
-// flight) and for the bf16 decode waves (8 fragments, one row block, bf16
-// tokens: still two waves per SIMD); else 2, which keeps wider operands (fp8,
-// fp32 tokens) and two row blocks at two waves per SIMD.
+// flight) and for the bf16 decode waves (8 fragments with one row block, 4
+// with two: still two waves per SIMD); else 2, which keeps wider operands
+// (fp8, fp32 tokens) at two waves per SIMD.
 constexpr int stream_depth(int fn, int mr, bool bf16_ops) {
-  return (fn == 2 || (fn == 8 && mr == 1 && bf16_ops)) ? 4 : 2;
+  return (fn == 2 || (bf16_ops && ((fn == 8 && mr == 1) || (fn == 4 && mr == 2)))) ? 4 : 2;
 }
 
 template <int MODE, typename AT, bool FP8, bool PACKED, int MR>
@@ -1823,9 +1823,11 @@ static void launch_stream(const Shape& s, const GemmArgs& g, hipStream_t st) {
   // about 1024 stream weights at once (one M-tile per expert at decode).
   while (fn > 2 && (long long)s.n_run * (g.N / (fn * per)) < 1024) fn /= 2;
   const int bm = stream_bm(s);
-  // fp8 operands take twice the registers of bf16: with two row blocks, 8
-  // fragments per wave would leave one wave per SIMD
-  if (FP8 && bm != kStreamBM && fn == 8) fn = 4;
+  // Two row blocks: 4 fragments per wave. With fp8 operands (twice the
+  // registers of bf16) 8 would leave one wave per SIMD; with bf16 tokens 4
+  // fragments and a 4-deep ring stream 1% faster at 384 and 512 tokens.
+  constexpr bool B16 = !FP8 && std::is_same<AT, uint16_t>::value;
+  if ((FP8 || B16) && bm != kStreamBM && fn == 8) fn = 4;
   dim3 grid(mtile_bound(s, bm) * (g.N / (fn * per)));
   if (bm == kStreamBM)
     launch_stream_mr<MODE, AT, FP8, PACKED, 1>(grid, fn, g, st);

@@ -97,7 +97,7 @@ def test_stream_variant_wide(packed):
 # 32-row M-tiles (two row blocks per weight fragment): experts of 17-32 rows
 # in one tile, hot experts over many tiles with a ragged last one.
 @pytest.mark.parametrize("name,T,H,I,x_dtype,w_dtype,bias,packed", [
-    ("bf16 8-fragment waves", 450, 1024, 512, "bf16", "bf16", "normal", False),
+    ("bf16 wide", 450, 1024, 512, "bf16", "bf16", "normal", False),
     ("bf16 packed hot", 400, 512, 256, "bf16", "bf16", "hot", True),
     ("fp32 x", 400, 256, 128, "f32", "bf16", "normal", True),
     ("fp8 rowmajor", 400, 512, 256, "bf16", "fp8", "normal", False),
